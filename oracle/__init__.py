@@ -1,0 +1,12 @@
+"""fp64 CPU oracle of the XAttention prefill path.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+bench's CPU-baseline leg, never by the library.
+"""
+from .xattn_oracle import (Selection, antidiagonal_sums, approx_attention, block_mass,
+                           block_scores, block_sparse_attention, find_blocks,
+                           full_attention, select_all, to_mask)
+
+__all__ = ["Selection", "antidiagonal_sums", "approx_attention", "block_mass",
+           "block_scores", "block_sparse_attention", "find_blocks", "full_attention",
+           "select_all", "to_mask"]

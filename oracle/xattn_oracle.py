@@ -1,0 +1,195 @@
+"""Plain float64 CPU oracle of the XAttention prefill path.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+CPU-baseline leg may import this module; the library never does, and it
+shares no code with the HIP kernels.  Everything here is numpy float64 on the
+exact input values, written to be checked against the pages by eye.
+
+Source: "XAttention: Block Sparse Attention with Antidiagonal Scoring"
+(papercache.org summary, section 2.2 "Threshold Block Selection": the
+find_blocks equation and Algorithm 1; the chapterpal.com page, Knowl 2, restates
+both in English).  The block-sparse attention step follows section 1 (step 3,
+"Block Sparse Attention") of the same summary and step 4 of the dtcms.com
+worked example (softmax over the selected entries at 1/sqrt(d)).
+
+Readings where the pages are silent (each is pinned by a test):
+  * "append" in Algorithm 1 concatenates along the feature axis, so a reshaped
+    query row pairs query sub-row a with key sub-row S-1-a: the product entry
+    is the sum of the S-th antidiagonal of one SxS tile of Q K^T.
+  * causal: reshaped column c is masked when c > R (reshaped row).  The
+    diagonal entry c == R keeps its whole antidiagonal.
+  * block mass = sum of A_approx over the (B/S)x(B/S) tile, divided by B/S so
+    every query-block row sums to 1 (tau lies in (0, 1]).
+  * find_blocks runs per (head, query block) over the valid key blocks
+    (kb <= qb when causal), in order of mass descending, lower kb first on
+    ties; the cut is the first prefix whose mass is >= tau; tau >= 1 (or a
+    tau never reached because of rounding) selects every valid block.
+  * sparse attention: softmax at 1/sqrt(d) renormalised over the keys of the
+    selected blocks (and j <= i when causal); a row with no key outputs 0.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Iterable, List, Optional, Sequence
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Step 1 -- strided antidiagonal sums (section 2.1 / 2.2; Algorithm 1's
+# reshape-and-multiply).  A[R, c] is the sum of the elements (i, j) of Q K^T
+# inside the SxS tile (R, c) that lie on its antidiagonal i + j = (R+c)S + S-1.
+# ---------------------------------------------------------------------------
+def antidiagonal_sums(Q: np.ndarray, K: np.ndarray, S: int,
+                      rows: Optional[range] = None) -> np.ndarray:
+    """A[R, c] = sum_{a<S} <Q[R*S + a], K[c*S + S-1-a]> for R in `rows`, all c.
+
+    Q: float64 (Lq, d), K: float64 (Lk, d) (the path uses Lq == Lk == L).  Written as the explicit tile-antidiagonal sum: the
+    query rows with phase a against the key rows with phase S-1-a.
+    """
+    rows = range(Q.shape[0] // S) if rows is None else rows
+    r0, r1 = rows.start, rows.stop
+    Lk = K.shape[0] // S
+    A = np.zeros((r1 - r0, Lk), dtype=np.float64)
+    for a in range(S):
+        q_phase = Q[r0 * S + a: r1 * S: S]          # rows R*S + a
+        k_phase = K[S - 1 - a: Lk * S: S]           # rows c*S + S-1-a
+        A += q_phase @ k_phase.T
+    return A
+
+
+# ---------------------------------------------------------------------------
+# Step 2 -- A_approx = Softmax(A / sqrt(d_h * S)) per reshaped row (Algorithm 1),
+# with the causal reading c > R masked.
+# ---------------------------------------------------------------------------
+def approx_attention(A: np.ndarray, d: int, S: int, causal: bool, row0: int) -> np.ndarray:
+    Z = A / math.sqrt(d * S)
+    if causal:
+        R = np.arange(row0, row0 + A.shape[0])[:, None]
+        c = np.arange(A.shape[1])[None, :]
+        Z = np.where(c > R, -np.inf, Z)
+    m = Z.max(axis=1, keepdims=True)
+    E = np.exp(Z - m)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Step 3 -- block mass: sum of A_approx over each (B/S)x(B/S) tile, / (B/S).
+# ---------------------------------------------------------------------------
+def block_mass(P: np.ndarray, B: int, S: int) -> np.ndarray:
+    """P: rows of whole query blocks (a multiple of B/S rows), L/S columns."""
+    bs = B // S
+    nq = P.shape[0] // bs
+    nk = P.shape[1] // bs
+    tiles = P[: nq * bs, : nk * bs].reshape(nq, bs, nk, bs)
+    return tiles.sum(axis=(1, 3)) / bs
+
+
+def block_scores(Q: np.ndarray, K: np.ndarray, S: int, B: int, causal: bool,
+                 qblocks: Optional[Sequence[int]] = None, chunk: int = 64) -> np.ndarray:
+    """Block scores [len(qblocks)][NB] of one head (Q: its queries, K: its group's keys).
+
+    Follows Algorithm 1 per query block b: reshaped product, scaled softmax,
+    then the tile sums that find_blocks takes.  Causal entries kb > qb are 0.
+    Consecutive query blocks are evaluated `chunk` at a time (their rows do
+    not interact).
+    """
+    L, d = Q.shape
+    NB = L // B
+    bs = B // S
+    qblocks = list(range(NB)) if qblocks is None else [int(b) for b in qblocks]
+    out = np.zeros((len(qblocks), NB), dtype=np.float64)
+    i = 0
+    while i < len(qblocks):
+        j = i + 1
+        while j < len(qblocks) and j - i < chunk and qblocks[j] == qblocks[j - 1] + 1:
+            j += 1
+        b0, b1 = qblocks[i], qblocks[j - 1] + 1
+        A = antidiagonal_sums(Q, K, S, range(b0 * bs, b1 * bs))
+        P = approx_attention(A, d, S, causal, b0 * bs)
+        out[i:j] = block_mass(P, B, S)
+        i = j
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Step 4 -- find_blocks(A, tau) = argmin_{blocks} |blocks| s.t. mass >= tau.
+# The smallest set reaching tau is a prefix of the blocks sorted by mass.
+# ---------------------------------------------------------------------------
+@dataclass
+class Selection:
+    selected: np.ndarray     # ascending key-block ids
+    kstar: int               # number selected
+    order: np.ndarray        # valid key blocks, mass descending, lower kb first on ties
+    csum: np.ndarray         # inclusive prefix sums of mass in `order` (float64)
+    n_valid: int
+
+    def prefix(self, k: int) -> float:
+        """P_k (P_0 = 0)."""
+        return 0.0 if k <= 0 else float(self.csum[k - 1])
+
+
+def find_blocks(mass_row: np.ndarray, n_valid: int, tau: float) -> Selection:
+    mass = np.asarray(mass_row, dtype=np.float64)[:n_valid]
+    kb = np.arange(n_valid)
+    order = np.lexsort((kb, -mass))          # primary: mass desc; secondary: kb asc
+    csum = np.cumsum(mass[order])            # sequential float64 accumulation
+    if tau >= 1.0:
+        k = n_valid
+    else:
+        hit = np.nonzero(csum >= tau)[0]
+        k = int(hit[0]) + 1 if hit.size else n_valid
+    sel = np.sort(order[:k])
+    return Selection(selected=sel, kstar=k, order=order, csum=csum, n_valid=n_valid)
+
+
+def select_all(scores: np.ndarray, causal: bool, tau: float,
+               qblocks: Optional[Sequence[int]] = None) -> List[Selection]:
+    """find_blocks for every row of `scores` (rows are query blocks `qblocks`)."""
+    NB = scores.shape[1]
+    qblocks = list(range(scores.shape[0])) if qblocks is None else list(qblocks)
+    return [find_blocks(scores[i], (qb + 1) if causal else NB, tau)
+            for i, qb in enumerate(qblocks)]
+
+
+def to_mask(sel: Selection, NB: int) -> np.ndarray:
+    """Bitmask words (uint64, bit kb % 64 of word kb // 64) of one selection."""
+    words = np.zeros((NB + 63) // 64, dtype=np.uint64)
+    for kb in sel.selected:
+        words[kb // 64] |= np.uint64(1) << np.uint64(kb % 64)
+    return words
+
+
+# ---------------------------------------------------------------------------
+# Step 5 -- attention restricted to the selected blocks (block-sparse attention).
+# ---------------------------------------------------------------------------
+def block_sparse_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, B: int,
+                           causal: bool, qb: int, kblocks: Iterable[int]) -> np.ndarray:
+    """Output rows of query block qb: softmax(q k^T / sqrt(d)) over the keys of
+    the blocks `kblocks` (and j <= i when causal), applied to V.  float64 [B][d]."""
+    d = Q.shape[1]
+    q = Q[qb * B:(qb + 1) * B]
+    kbs = sorted(set(int(k) for k in kblocks))
+    if not kbs:
+        return np.zeros((B, V.shape[1]))
+    keys = np.concatenate([np.arange(kb * B, (kb + 1) * B) for kb in kbs])
+    logits = (q @ K[keys].T) / math.sqrt(d)
+    if causal:
+        i = np.arange(qb * B, (qb + 1) * B)[:, None]
+        logits = np.where(keys[None, :] > i, -np.inf, logits)
+    m = logits.max(axis=1, keepdims=True)
+    live = np.isfinite(m[:, 0])
+    m = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(logits - m)
+    den = w.sum(axis=1, keepdims=True)
+    out = (w @ V[keys]) / np.where(den > 0, den, 1.0)
+    out[~live] = 0.0
+    return out
+
+
+def full_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, B: int, causal: bool,
+                   qb: int) -> np.ndarray:
+    """Dense attention for the rows of query block qb (all keys, j <= i if causal)."""
+    NB = Q.shape[0] // B
+    return block_sparse_attention(Q, K, V, B, causal, qb, range(qb + 1 if causal else NB))
