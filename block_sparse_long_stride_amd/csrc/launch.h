@@ -1,0 +1,45 @@
+// Host-side launchers of the libxattn kernels.  Arguments are validated by
+// the C-ABI layer (xattn_api.cpp) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace xattn {
+
+struct Shape {
+  int hq, hkv, L, d, causal;
+  bool bf16;
+};
+
+// ---- block scores ---------------------------------------------------------
+// Workspace of the bf16 scoring path: per (head, 32-row group of reshaped rows)
+//   P: [NB][32] fp32 partial block sums (each against its own snapshot max)
+//   M: [nct][32] fp32 snapshot max (log2 units) per 64-column range
+//   Z: [nct][32] fp32 snapshot sum of exp2 against that max
+size_t score_workspace_bytes(const Shape& s, int S, int B);
+hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
+                             float* scores, void* ws, hipStream_t st);
+hipError_t launch_score_fp32(const Shape& s, const void* Q, const void* K, int S, int B,
+                             float* scores, hipStream_t st);
+
+// ---- selection --------------------------------------------------------------
+constexpr int kMaxHeads = 128;
+constexpr int kMaxSelectBlocks = 4096;
+struct TauArray {
+  float v[kMaxHeads];
+};
+hipError_t launch_select(int hq, int NB, int causal, const float* scores, const TauArray& tau,
+                         uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
+
+// ---- attention ---------------------------------------------------------------
+// idx == nullptr selects dense mode (every key block, causal-limited).
+hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const void* V,
+                             int B, const int32_t* idx, const int32_t* counts, void* O,
+                             hipStream_t st);
+hipError_t launch_flash_fp32(const Shape& s, const void* Q, const void* K, const void* V,
+                             int B, const int32_t* idx, const int32_t* counts, void* O,
+                             hipStream_t st);
+
+}  // namespace xattn

@@ -1,0 +1,387 @@
+// Block scores of XAttention ("XAttention: Block Sparse Attention with
+// Antidiagonal Scoring", papercache.org summary, section 2.2, Algorithm 1)
+// for bf16 inputs on gfx950.
+//
+// Algorithm 1 multiplies a stride-S reshape of the queries (phases S-1 .. 0
+// appended along features) by a reshape of the keys (phases 0 .. S-1).  The
+// product entry (R, c) is sum_a <Q[R*S+a], K[c*S+S-1-a]>: the antidiagonal sum
+// of the SxS tile (R, c) of Q K^T.  Here it is one GEMM with M = N = L/S and
+// K-dimension S*d: the query operand is Q's own memory read as an (L/S) x (S*d)
+// matrix, and the key operand reads sub-row S-1-a of key group c for feature
+// chunk a -- the reshape is folded into the global load addresses and never
+// materialised.
+//
+// Kernel 1 (score_gemm): MFMA 32x32x16 bf16 GEMM over lower-triangular (causal)
+// or all 128x128 tiles of the reshaped matrix, computed transposed (rows =
+// key columns c, columns = query rows R) so that each lane owns one reshaped
+// row R.  Its epilogue masks c > R, scales by log2(e)/sqrt(d*S) and, per
+// 64-column range of each row, writes the range max m, the range sum of
+// exp2(z - m) and the per-key-block sums of exp2(z - m).  The (L/S)^2 matrix
+// never reaches HBM.
+// Kernel 2 (score_fixup): per 32 reshaped rows, combines the range snapshots
+// into the row's softmax max and denominator, rescales the partial block sums,
+// adds the B/S rows of each query block and divides by B/S.
+#include "common.h"
+#include "launch.h"
+
+namespace xattn {
+namespace {
+
+constexpr int kTile = 128;       // reshaped rows / columns per workgroup tile
+constexpr int kWaveCols = 64;    // columns per wave (and per softmax snapshot)
+constexpr int kKC = 32;          // reduction chunk (elements of S*d)
+constexpr int kPad = 8;          // LDS row padding (elements)
+constexpr int kLdsRow = kKC + kPad;
+
+struct GemmParams {
+  const uint16_t* Q;
+  const uint16_t* K;
+  float* P;   // [hq][nR32][NB][32]
+  float* M;   // [hq][nR32][nct][32]
+  float* Z;   // [hq][nR32][nct][32]
+  int L, S, group, NB, Lr, nR32, nct;
+  int causal, nt, tiles_per_head, nwork, grid;
+  float scale_log2;
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(256) void score_gemm(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kTile * kLdsRow];
+
+  const int w = xcd_swizzle(blockIdx.x, p.grid);
+  if (w >= p.nwork) return;
+  // work order: (kv group, tile, query head within group), heads fastest
+  const int hh = w % p.group;
+  const int t = (w / p.group) % p.tiles_per_head;
+  const int g = w / (p.group * p.tiles_per_head);
+  const int h = g * p.group + hh;
+  int tr, tc;
+  if (p.causal) {
+    tr = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+    while (tr * (tr + 1) / 2 > t) --tr;
+    tc = t - tr * (tr + 1) / 2;
+  } else {
+    tr = t / p.nt;
+    tc = t % p.nt;
+  }
+  const int R0 = tr * kTile, C0 = tc * kTile;
+  const int F = p.S * D;
+  const int Lr = p.Lr;
+  const uint16_t* Qh = p.Q + (size_t)h * p.L * D;
+  const uint16_t* Kg = p.K + (size_t)g * p.L * D;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wc = wave & 1, wr = wave >> 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // global -> register staging: 2 rows of Q and 2 rows of K' per thread
+  const int lrow = tid >> 2, lcol = (tid & 3) * 8;
+  u32x4_t rq[2], rk[2];
+  auto load_chunk = [&](int kc) {
+    const int f0 = kc * kKC;
+    const int a = f0 / D, e0 = f0 % D;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int R = R0 + i * 64 + lrow;
+      const int C = C0 + i * 64 + lrow;
+      rq[i] = (R < Lr) ? *(const u32x4_t*)(Qh + (size_t)R * F + f0 + lcol) : u32x4_t{0, 0, 0, 0};
+      rk[i] = (C < Lr) ? *(const u32x4_t*)(Kg + ((size_t)C * p.S + (p.S - 1 - a)) * D + e0 + lcol)
+                       : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *(u32x4_t*)&sQ[buf][(i * 64 + lrow) * kLdsRow + lcol] = rq[i];
+      *(u32x4_t*)&sK[buf][(i * 64 + lrow) * kLdsRow + lcol] = rk[i];
+    }
+  };
+
+  // a wave whose whole column range lies right of its last row is fully masked
+  const bool wave_live = !p.causal || (C0 + wc * kWaveCols <= R0 + wr * 64 + 63);
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int nk = F / kKC;
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nk) load_chunk(kc + 1);
+    if (wave_live) {
+#pragma unroll
+      for (int ks = 0; ks < kKC / 16; ++ks) {
+        bf16x8_t af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          af[i] = as_bf16x8(*(const u32x4_t*)&sK[buf][(wc * 64 + i * 32 + l32) * kLdsRow + ks * 16 + hi * 8]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[j] = as_bf16x8(*(const u32x4_t*)&sQ[buf][(wr * 64 + j * 32 + l32) * kLdsRow + ks * 16 + hi * 8]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
+      }
+    }
+    if (kc + 1 < nk) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+  if (!wave_live) return;
+
+  // ---- epilogue: per reshaped row R (one per lane and R-tile) ---------------
+  const int cw = C0 + wc * kWaveCols;   // first column of this wave's range
+  const int ct = cw / kWaveCols;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int R = R0 + wr * 64 + j * 32 + l32;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int c = cw + i * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
+        float z = acc[i][j][v] * p.scale_log2;
+        if (c >= Lr || (p.causal && c > R)) z = -INFINITY;
+        acc[i][j][v] = z;
+        m = fmaxf(m, z);
+      }
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float s[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float acc4 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = acc[i][j][4 * q + r];
+          acc4 += (z == -INFINITY) ? 0.f : fast_exp2(z - m);
+        }
+        s[i][q] = acc4;
+      }
+    float zsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zsum += s[i][q];
+    zsum += __shfl_xor(zsum, 32);
+    // Stores are guarded rather than branched around so that every lane takes
+    // part in the exchanges below.  A wave range starting at or past Lr (the
+    // ragged last tile) owns no snapshot slot.
+    const bool row_ok = R < Lr && cw < Lr;
+    const size_t rowbase = (size_t)h * p.nR32 + (R >> 5);
+    if (row_ok && hi == 0) {
+      p.M[(rowbase * p.nct + ct) * 32 + (R & 31)] = m;
+      p.Z[(rowbase * p.nct + ct) * 32 + (R & 31)] = zsum;
+    }
+    float* Prow = p.P + rowbase * p.NB * 32 + (R & 31);
+    const int kb0 = cw / BS;
+    if constexpr (BS == 4) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kb = kb0 + 8 * i + 2 * q + hi;
+          if (row_ok && kb < p.NB) Prow[(size_t)kb * 32] = s[i][q];
+        }
+    } else if constexpr (BS == 8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float tot = s[i][q] + __shfl_xor(s[i][q], 32);
+          const int kb = kb0 + 4 * i + q;
+          if (row_ok && (q & 1) == hi && kb < p.NB) Prow[(size_t)kb * 32] = tot;
+        }
+    } else if constexpr (BS == 16) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; q += 2) {
+          float tot = s[i][q] + s[i][q + 1];
+          tot += __shfl_xor(tot, 32);
+          const int kb = kb0 + 2 * i + q / 2;
+          if (row_ok && ((q >> 1) & 1) == hi && kb < p.NB) Prow[(size_t)kb * 32] = tot;
+        }
+    } else {  // BS == 32
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float tot = s[i][0] + s[i][1] + s[i][2] + s[i][3];
+        tot += __shfl_xor(tot, 32);
+        const int kb = kb0 + i;
+        if (row_ok && i == hi && kb < p.NB) Prow[(size_t)kb * 32] = tot;
+      }
+    }
+  }
+}
+
+struct FixupParams {
+  const float* P;
+  const float* M;
+  const float* Z;
+  float* scores;   // [hq][NB][NB]
+  int hq, NB, Lr, nR32, nct, bs, causal;
+};
+
+// One workgroup per (head, 32 reshaped rows).
+__global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
+  __shared__ float s_mfin[32];
+  __shared__ float s_invz[32];
+  const int h = blockIdx.x / p.nR32;
+  const int rg = blockIdx.x % p.nR32;
+  const int tid = threadIdx.x;
+  const size_t rowbase = (size_t)h * p.nR32 + rg;
+  const float* M = p.M + rowbase * p.nct * 32;
+  const float* Z = p.Z + rowbase * p.nct * 32;
+  const float* P = p.P + rowbase * p.NB * 32;
+
+  // 1. per row: softmax max and denominator from the range snapshots
+  {
+    const int r = tid >> 3, sub = tid & 7;
+    const int R = rg * 32 + r;
+    int nct_r = p.nct;
+    if (p.causal) {
+      const int last = (R / p.bs + 1) * p.bs - 1;   // last row of R's query block
+      nct_r = min(p.nct, last / kWaveCols + 1);
+    }
+    float m = -INFINITY;
+    if (R < p.Lr)
+      for (int c = sub; c < nct_r; c += 8) m = fmaxf(m, M[c * 32 + r]);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float z = 0.f;
+    if (R < p.Lr && m != -INFINITY)
+      for (int c = sub; c < nct_r; c += 8) {
+        const float mc = M[c * 32 + r];
+        if (mc != -INFINITY) z += Z[c * 32 + r] * fast_exp2(mc - m);
+      }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) z += __shfl_xor(z, o);
+    if (sub == 0) {
+      s_mfin[r] = m;
+      s_invz[r] = (z > 0.f) ? 1.0f / z : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // 2. block scores for the 32/bs query blocks of this row group
+  const int nq = 32 / p.bs;
+  const int qb0 = rg * nq;
+  const float inv_bs = 1.0f / (float)p.bs;
+  for (int it = tid; it < nq * p.NB; it += blockDim.x) {
+    const int kb = it / nq, q = it % nq;
+    const int qb = qb0 + q;
+    if (qb >= p.NB) continue;
+    float out = 0.f;
+    if (!p.causal || kb <= qb) {
+      const int c = (kb * p.bs) / kWaveCols;
+      float acc = 0.f;
+      for (int r = q * p.bs; r < (q + 1) * p.bs; ++r) {
+        const float mc = M[c * 32 + r];
+        if (mc == -INFINITY) continue;
+        acc += P[(size_t)kb * 32 + r] * fast_exp2(mc - s_mfin[r]) * s_invz[r];
+      }
+      out = acc * inv_bs;
+    }
+    p.scores[((size_t)h * p.NB + qb) * p.NB + kb] = out;
+  }
+}
+
+template <int D, int BS>
+hipError_t launch_gemm(const GemmParams& gp, hipStream_t st) {
+  hipLaunchKernelGGL((score_gemm<D, BS>), dim3(gp.grid), dim3(256), 0, st, gp);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_gemm_bs(const GemmParams& gp, int bs, hipStream_t st) {
+  switch (bs) {
+    case 4: return launch_gemm<D, 4>(gp, st);
+    case 8: return launch_gemm<D, 8>(gp, st);
+    case 16: return launch_gemm<D, 16>(gp, st);
+    case 32: return launch_gemm<D, 32>(gp, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+struct WsLayout {
+  size_t p_elems, m_elems;
+  int Lr, NB, nR32, nct;
+};
+
+WsLayout ws_layout(const Shape& s, int S, int B) {
+  WsLayout w;
+  w.Lr = s.L / S;
+  w.NB = s.L / B;
+  w.nR32 = (w.Lr + 31) / 32;
+  w.nct = (w.Lr + kWaveCols - 1) / kWaveCols;
+  w.p_elems = (size_t)s.hq * w.nR32 * w.NB * 32;
+  w.m_elems = (size_t)s.hq * w.nR32 * w.nct * 32;
+  return w;
+}
+
+}  // namespace
+
+size_t score_workspace_bytes(const Shape& s, int S, int B) {
+  if (!s.bf16) return 0;
+  const WsLayout w = ws_layout(s, S, B);
+  return (w.p_elems + 2 * w.m_elems) * sizeof(float);
+}
+
+hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
+                             float* scores, void* ws, hipStream_t st) {
+  const WsLayout wl = ws_layout(s, S, B);
+  float* P = (float*)ws;
+  float* M = P + wl.p_elems;
+  float* Z = M + wl.m_elems;
+
+  GemmParams gp;
+  gp.Q = (const uint16_t*)Q;
+  gp.K = (const uint16_t*)K;
+  gp.P = P;
+  gp.M = M;
+  gp.Z = Z;
+  gp.L = s.L;
+  gp.S = S;
+  gp.group = s.hq / s.hkv;
+  gp.NB = wl.NB;
+  gp.Lr = wl.Lr;
+  gp.nR32 = wl.nR32;
+  gp.nct = wl.nct;
+  gp.causal = s.causal;
+  gp.nt = (wl.Lr + kTile - 1) / kTile;
+  gp.tiles_per_head = s.causal ? gp.nt * (gp.nt + 1) / 2 : gp.nt * gp.nt;
+  gp.nwork = gp.tiles_per_head * s.hq;
+  gp.grid = (gp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
+  gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
+  const int bs = B / S;
+  hipError_t e = (s.d == 128) ? launch_gemm_bs<128>(gp, bs, st) : launch_gemm_bs<64>(gp, bs, st);
+  if (e != hipSuccess) return e;
+
+  FixupParams fp;
+  fp.P = P;
+  fp.M = M;
+  fp.Z = Z;
+  fp.scores = scores;
+  fp.hq = s.hq;
+  fp.NB = wl.NB;
+  fp.Lr = wl.Lr;
+  fp.nR32 = wl.nR32;
+  fp.nct = wl.nct;
+  fp.bs = bs;
+  fp.causal = s.causal;
+  hipLaunchKernelGGL(score_fixup, dim3(s.hq * wl.nR32), dim3(256), 0, st, fp);
+  return hipGetLastError();
+}
+
+}  // namespace xattn

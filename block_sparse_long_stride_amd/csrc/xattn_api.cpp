@@ -1,0 +1,206 @@
+// C-ABI of libxattn: argument validation and dispatch to the gfx950 kernels.
+// Every check runs before the first HIP call, so malformed calls return an
+// error without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/xattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+xattn_status fail(xattn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+xattn_status fail(xattn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+xattn_status ok() {
+  g_last_error.clear();
+  return XATTN_OK;
+}
+
+xattn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(XATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+xattn_status check_shape(const xattn_shape* s, xattn::Shape* out) {
+  if (!s) return fail(XATTN_EINVAL, "shape is NULL");
+  if (s->hq < 1 || s->hkv < 1 || s->L < 1 || s->d < 1)
+    return fail(XATTN_EINVAL, "shape fields must be >= 1 (hq=%d hkv=%d L=%d d=%d)", s->hq, s->hkv,
+                s->L, s->d);
+  if (s->hq % s->hkv)
+    return fail(XATTN_EINVAL, "hq (%d) must be a multiple of hkv (%d)", s->hq, s->hkv);
+  if (s->dtype != XATTN_FP32 && s->dtype != XATTN_BF16)
+    return fail(XATTN_EINVAL, "dtype %d is neither XATTN_FP32 nor XATTN_BF16", s->dtype);
+  if (s->causal != 0 && s->causal != 1) return fail(XATTN_EINVAL, "causal must be 0 or 1");
+  const long long elems = (long long)s->hq * s->L * s->d;
+  if (elems >= (1ll << 40)) return fail(XATTN_EUNSUPPORTED, "tensor too large");
+  out->hq = s->hq;
+  out->hkv = s->hkv;
+  out->L = s->L;
+  out->d = s->d;
+  out->causal = s->causal;
+  out->bf16 = s->dtype == XATTN_BF16;
+  return XATTN_OK;
+}
+
+xattn_status check_score_args(const xattn_shape* shape, int S, int B, xattn::Shape* s) {
+  xattn_status st = check_shape(shape, s);
+  if (st != XATTN_OK) return st;
+  if (S < 1 || B < 1) return fail(XATTN_EINVAL, "S (%d) and B (%d) must be >= 1", S, B);
+  if (s->L % B) return fail(XATTN_EINVAL, "L (%d) must be a multiple of B (%d)", s->L, B);
+  if (B % S) return fail(XATTN_EINVAL, "B (%d) must be a multiple of S (%d)", B, S);
+  const int bs = B / S;
+  if (s->bf16) {
+    if (s->d != 64 && s->d != 128)
+      return fail(XATTN_EUNSUPPORTED, "bf16 scoring covers d in {64, 128}, got %d", s->d);
+    if (bs != 4 && bs != 8 && bs != 16 && bs != 32)
+      return fail(XATTN_EUNSUPPORTED, "bf16 scoring covers B/S in {4, 8, 16, 32}, got %d", bs);
+  } else {
+    if (s->d > 1024) return fail(XATTN_EUNSUPPORTED, "fp32 scoring covers d <= 1024");
+    if (bs > 256) return fail(XATTN_EUNSUPPORTED, "fp32 scoring covers B/S <= 256");
+  }
+  return XATTN_OK;
+}
+
+xattn_status check_attn_args(const xattn::Shape& s, int B) {
+  if (B < 1) return fail(XATTN_EINVAL, "B (%d) must be >= 1", B);
+  if (s.L % B) return fail(XATTN_EINVAL, "L (%d) must be a multiple of B (%d)", s.L, B);
+  if (s.bf16) {
+    if (s.d != 64 && s.d != 128)
+      return fail(XATTN_EUNSUPPORTED, "bf16 attention covers d in {64, 128}, got %d", s.d);
+    if (B != 64 && B != 128)
+      return fail(XATTN_EUNSUPPORTED, "bf16 attention covers B in {64, 128}, got %d", B);
+  } else {
+    if (s.d != 32 && s.d != 64 && s.d != 128)
+      return fail(XATTN_EUNSUPPORTED, "fp32 attention covers d in {32, 64, 128}, got %d", s.d);
+    if (B > 256) return fail(XATTN_EUNSUPPORTED, "fp32 attention covers B <= 256, got %d", B);
+  }
+  return XATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t B) {
+  xattn::Shape s;
+  std::string saved = g_last_error;
+  if (check_score_args(shape, S, B, &s) != XATTN_OK) {
+    g_last_error = saved;
+    return 0;
+  }
+  return xattn::score_workspace_bytes(s, S, B);
+}
+
+xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
+                         int32_t B, float* scores, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  xattn::Shape s;
+  xattn_status st = check_score_args(shape, S, B, &s);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !scores) return fail(XATTN_EINVAL, "Q, K and scores must be non-NULL");
+  const size_t need = xattn::score_workspace_bytes(s, S, B);
+  if (need && !workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(XATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = s.bf16 ? xattn::launch_score_bf16(s, Q, K, S, B, scores, workspace, hs)
+                        : xattn::launch_score_fp32(s, Q, K, S, B, scores, hs);
+  return hip_status(e, "xattn_score launch");
+}
+
+xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                          const float* tau_host, uint64_t* mask, int32_t* idx, int32_t* counts,
+                          void* stream) {
+  if (hq < 1 || NB < 1) return fail(XATTN_EINVAL, "hq (%d) and NB (%d) must be >= 1", hq, NB);
+  if (causal != 0 && causal != 1) return fail(XATTN_EINVAL, "causal must be 0 or 1");
+  if (!scores || !tau_host || !mask || !idx || !counts)
+    return fail(XATTN_EINVAL, "scores, tau_host, mask, idx and counts must be non-NULL");
+  if (hq > xattn::kMaxHeads)
+    return fail(XATTN_EUNSUPPORTED, "selection covers hq <= %d, got %d", xattn::kMaxHeads, hq);
+  if (NB > xattn::kMaxSelectBlocks)
+    return fail(XATTN_EUNSUPPORTED, "selection covers NB <= %d, got %d", xattn::kMaxSelectBlocks, NB);
+  xattn::TauArray tau;
+  for (int h = 0; h < xattn::kMaxHeads; ++h) tau.v[h] = 1.0f;
+  for (int h = 0; h < hq; ++h) {
+    const float t = tau_host[h];
+    if (!(t > 0.0f && t <= 1.0f))
+      return fail(XATTN_EINVAL, "tau[%d] = %g is outside (0, 1]", h, (double)t);
+    tau.v[h] = t;
+  }
+  hipError_t e = xattn::launch_select(hq, NB, causal, scores, tau, mask, idx, counts,
+                                      (hipStream_t)stream);
+  return hip_status(e, "xattn_select launch");
+}
+
+xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
+                                  const void* V, int32_t B, const int32_t* idx,
+                                  const int32_t* counts, void* O, void* stream) {
+  xattn::Shape s;
+  xattn_status st = check_shape(shape, &s);
+  if (st != XATTN_OK) return st;
+  st = check_attn_args(s, B);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !V || !O || !idx || !counts)
+    return fail(XATTN_EINVAL, "Q, K, V, O, idx and counts must be non-NULL");
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = s.bf16 ? xattn::launch_flash_bf16(s, Q, K, V, B, idx, counts, O, hs)
+                        : xattn::launch_flash_fp32(s, Q, K, V, B, idx, counts, O, hs);
+  return hip_status(e, "xattn_sparse_prefill launch");
+}
+
+xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K, const void* V,
+                        void* O, void* stream) {
+  xattn::Shape s;
+  xattn_status st = check_shape(shape, &s);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !V || !O) return fail(XATTN_EINVAL, "Q, K, V and O must be non-NULL");
+  int B = 0;
+  if (s.bf16) {
+    B = (s.L % 128 == 0) ? 128 : (s.L % 64 == 0 ? 64 : 0);
+    if (!B) return fail(XATTN_EUNSUPPORTED, "bf16 dense attention needs L %% 64 == 0, got %d", s.L);
+  } else {
+    for (int b = 128; b >= 1; b >>= 1)
+      if (s.L % b == 0) {
+        B = b;
+        break;
+      }
+  }
+  st = check_attn_args(s, B);
+  if (st != XATTN_OK) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = s.bf16 ? xattn::launch_flash_bf16(s, Q, K, V, B, nullptr, nullptr, O, hs)
+                        : xattn::launch_flash_fp32(s, Q, K, V, B, nullptr, nullptr, O, hs);
+  return hip_status(e, "xattn_full launch");
+}
+
+const char* xattn_status_str(xattn_status status) {
+  switch (status) {
+    case XATTN_OK: return "ok";
+    case XATTN_EINVAL: return "invalid argument";
+    case XATTN_EUNSUPPORTED: return "unsupported shape or parameter";
+    case XATTN_EWORKSPACE: return "workspace too small";
+    case XATTN_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* xattn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t xattn_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+"""Python binding of libxattn (ctypes).
+
+Argument marshalling only: torch tensors supply device pointers, the current
+HIP stream supplies the stream, and every step of the path runs in the
+library's HIP kernels.  Functions keep the C names.  If libxattn.so is missing
+the functions raise; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so")
+
+XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EWORKSPACE, XATTN_EHIP = range(5)
+XATTN_FP32, XATTN_BF16 = 0, 1
+
+# every entry point declared in include/xattn.h
+EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_select",
+           "xattn_sparse_prefill", "xattn_full", "xattn_status_str", "xattn_last_error",
+           "xattn_version")
+
+
+class XattnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where} failed with status {status}: {detail}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libxattn.so (built in-tree by block_sparse_long_stride_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m block_sparse_long_stride_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SP = ctypes.POINTER(Shape)
+    L.xattn_score_workspace_bytes.argtypes = [SP, I32, I32]
+    L.xattn_score_workspace_bytes.restype = SZ
+    L.xattn_score.argtypes = [SP, P, P, I32, I32, P, P, SZ, P]
+    L.xattn_score.restype = I32
+    L.xattn_select.argtypes = [I32, I32, I32, P, P, P, P, P, P]
+    L.xattn_select.restype = I32
+    L.xattn_sparse_prefill.argtypes = [SP, P, P, P, I32, P, P, P, P]
+    L.xattn_sparse_prefill.restype = I32
+    L.xattn_full.argtypes = [SP, P, P, P, P, P]
+    L.xattn_full.restype = I32
+    L.xattn_status_str.argtypes = [I32]
+    L.xattn_status_str.restype = ctypes.c_char_p
+    L.xattn_last_error.argtypes = []
+    L.xattn_last_error.restype = ctypes.c_char_p
+    L.xattn_version.argtypes = []
+    L.xattn_version.restype = I32
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != XATTN_OK:
+        raise XattnError(status, where, lib().xattn_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def shape_of(Q, K, causal: bool) -> Shape:
+    torch = _torch()
+    if Q.dim() != 3 or K.dim() != 3:
+        raise ValueError("Q must be [hq][L][d] and K [hkv][L][d]")
+    if Q.dtype == torch.bfloat16:
+        dt = XATTN_BF16
+    elif Q.dtype == torch.float32:
+        dt = XATTN_FP32
+    else:
+        raise ValueError(f"unsupported dtype {Q.dtype}")
+    if K.dtype != Q.dtype or Q.shape[1:] != K.shape[1:]:
+        raise ValueError("Q and K must share dtype, L and d")
+    for t in (Q, K):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+    return Shape(Q.shape[0], K.shape[0], Q.shape[1], Q.shape[2], dt, int(bool(causal)))
+
+
+def xattn_score_workspace_bytes(shape: Shape, S: int, B: int) -> int:
+    return int(lib().xattn_score_workspace_bytes(ctypes.byref(shape), S, B))
+
+
+def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None, stream=None):
+    """Block scores, fp32 [hq][NB][NB]."""
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    NB = sh.L // B if B > 0 else 0
+    if scores is None:
+        scores = torch.empty((sh.hq, NB, NB), dtype=torch.float32, device=Q.device)
+    need = xattn_score_workspace_bytes(sh, S, B)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().xattn_score(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B, _ptr(scores),
+                             _ptr(workspace), ws_bytes, _stream(stream)), "xattn_score")
+    return scores
+
+
+def xattn_select(scores, tau: Sequence[float], causal: bool, mask=None, idx=None, counts=None,
+                 stream=None) -> Tuple:
+    """(mask uint64-as-int64 [hq][NB][words], idx int32 [hq][NB][NB], counts int32 [hq][NB])."""
+    torch = _torch()
+    import numpy as np
+    hq, NB = scores.shape[0], scores.shape[1]
+    if not (scores.is_cuda and scores.is_contiguous() and scores.dtype == torch.float32):
+        raise ValueError("scores must be a contiguous fp32 device tensor")
+    tau_np = np.ascontiguousarray(np.broadcast_to(np.asarray(tau, dtype=np.float32), (hq,)))
+    words = (NB + 63) // 64
+    if mask is None:
+        mask = torch.empty((hq, NB, words), dtype=torch.int64, device=scores.device)
+    if idx is None:
+        idx = torch.empty((hq, NB, NB), dtype=torch.int32, device=scores.device)
+    if counts is None:
+        counts = torch.empty((hq, NB), dtype=torch.int32, device=scores.device)
+    _check(lib().xattn_select(hq, NB, int(bool(causal)), _ptr(scores),
+                              tau_np.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(idx),
+                              _ptr(counts), _stream(stream)), "xattn_select")
+    return mask, idx, counts
+
+
+def xattn_sparse_prefill(Q, K, V, B: int, idx, counts, causal: bool, out=None, stream=None):
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
+        raise ValueError("V must match K")
+    if out is None:
+        out = torch.empty_like(Q)
+    _check(lib().xattn_sparse_prefill(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), B, _ptr(idx),
+                                      _ptr(counts), _ptr(out), _stream(stream)),
+           "xattn_sparse_prefill")
+    return out
+
+
+def xattn_full(Q, K, V, causal: bool, out=None, stream=None):
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
+        raise ValueError("V must match K")
+    if out is None:
+        out = torch.empty_like(Q)
+    _check(lib().xattn_full(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
+                            _stream(stream)), "xattn_full")
+    return out

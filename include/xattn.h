@@ -1,0 +1,139 @@
+/*
+ * libxattn -- XAttention prefill path for AMD Instinct MI355X (gfx950).
+ *
+ * The method: "XAttention: Block Sparse Attention with Antidiagonal Scoring"
+ * (papercache.org summary).  Section 2.2 ("Threshold Block Selection") defines
+ * the problem this library solves: given Q, K in R^{L x d}, block size B,
+ * stride S, head dimension d_h and threshold tau, produce a block mask M
+ * (Algorithm 1 and the find_blocks equation); section 1 step 3 ("Block Sparse
+ * Attention") then computes attention over the selected blocks only.
+ *
+ * Calls, in the order of the path:
+ *   xattn_score          block scores from strided antidiagonal sums
+ *   xattn_select         threshold block selection -> mask, index lists
+ *   xattn_sparse_prefill attention over the selected blocks
+ *   xattn_full           dense attention (the speed baseline)
+ *
+ * Conventions for every call:
+ *   - Batch 1.  Q and O are [hq][L][d], K and V are [hkv][L][d], contiguous
+ *     row-major, dtype = shape->dtype (bf16 or fp32), 16-byte aligned device
+ *     memory.  Query head h reads key/value head h / (hq / hkv).
+ *   - Every pointer except `tau_host` and `shape` is device memory owned by
+ *     the caller.  The library allocates nothing, frees nothing and keeps no
+ *     pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *     work on that stream and never synchronise the host.
+ *   - Arguments are validated before any HIP call.  A call that returns an
+ *     error has enqueued nothing, except XATTN_EHIP (a launch failed).
+ *     xattn_last_error() returns a thread-local description of the last
+ *     error.  No C++ exception crosses this interface.
+ *   - Calls keep no global state and are safe to issue from several host
+ *     threads; calls on one stream run in order.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum xattn_status {
+  XATTN_OK = 0,
+  XATTN_EINVAL = 1,       /* malformed argument (null pointer, bad shape, tau) */
+  XATTN_EUNSUPPORTED = 2, /* well-formed, but outside what the kernels cover */
+  XATTN_EWORKSPACE = 3,   /* workspace smaller than xattn_score_workspace_bytes */
+  XATTN_EHIP = 4          /* a HIP launch reported an error */
+} xattn_status;
+
+typedef enum xattn_dtype { XATTN_FP32 = 0, XATTN_BF16 = 1 } xattn_dtype;
+
+typedef struct xattn_shape {
+  int32_t hq;     /* query heads, >= 1 */
+  int32_t hkv;    /* key/value heads, >= 1, hq % hkv == 0 */
+  int32_t L;      /* tokens, >= 1 */
+  int32_t d;      /* head dimension */
+  int32_t dtype;  /* xattn_dtype of Q, K, V and O */
+  int32_t causal; /* 1: token i attends to keys j <= i; 0: bidirectional */
+} xattn_shape;
+
+/* Bytes of device workspace xattn_score needs for this shape (0 if none).
+ * Returns 0 as well for arguments xattn_score would reject. */
+size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t B);
+
+/*
+ * Block scores (Algorithm 1 and section 2.1 "antidiagonal selection").
+ * For query head h, the stride-S reshape pairs query row R*S+a with key row
+ * c*S+S-1-a, so entry (R, c) of Q_reshaped K_reshaped^T is the sum of the
+ * antidiagonal of the SxS tile (R, c) of Q K^T.  Each reshaped row R gets a
+ * softmax over the L/S columns at scale 1/sqrt(d*S); when causal, columns
+ * c > R are excluded.  The block score of (query block qb, key block kb) is
+ * the sum of those probabilities over the (B/S)x(B/S) tile divided by B/S,
+ * so every query-block row sums to 1.
+ *
+ *   scores     out, fp32 [hq][NB][NB], NB = L / B.  Fully overwritten;
+ *              entries kb > qb are 0 when causal.
+ *   workspace  device scratch of at least xattn_score_workspace_bytes().
+ * Requires L % B == 0 and B % S == 0 (else XATTN_EINVAL).  bf16 kernels
+ * cover d in {64, 128} and B/S in {4, 8, 16, 32}; fp32 kernels cover d <= 128
+ * (else XATTN_EUNSUPPORTED).
+ */
+xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
+                         int32_t S, int32_t B, float* scores, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Threshold block selection: find_blocks(A, tau) of section 2.2, per (head,
+ * query block), over the valid key blocks (kb <= qb when causal, all NB
+ * otherwise).  Blocks are ranked by score, highest first, lower kb first on
+ * equal scores; the selection is the shortest prefix whose score sum
+ * (accumulated in float64) is >= tau[h].  tau[h] == 1, or a tau the prefix
+ * sums never reach, selects every valid block.
+ *
+ *   scores    in, fp32 [hq][NB][NB] (as written by xattn_score)
+ *   tau_host  in, HOST array of hq floats, each in (0, 1] (else XATTN_EINVAL)
+ *   mask      out, uint64 [hq][NB][(NB+63)/64]: bit kb%64 of word kb/64
+ *   idx       out, int32 [hq][NB][NB]: selected kb in ascending order, then -1
+ *   counts    out, int32 [hq][NB]: number of selected blocks (>= 1)
+ * Covers NB <= 4096 and hq <= 128 (else XATTN_EUNSUPPORTED).
+ */
+xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                          const float* tau_host, uint64_t* mask, int32_t* idx,
+                          int32_t* counts, void* stream);
+
+/*
+ * Block-sparse attention (section 1, step 3): for query block qb of head h,
+ * token i attends to the keys of the blocks idx[h][qb][0 .. counts[h][qb]),
+ * intersected with j <= i when causal; softmax at scale 1/sqrt(d) over those
+ * keys only, applied to V.
+ *
+ *   idx, counts  in, as written by xattn_select.  Entries outside [0, NB)
+ *                and, when causal, entries > qb are ignored; counts are
+ *                clamped to [0, NB].  A row with no key gets O = 0.
+ *   O            out, [hq][L][d] in the input dtype, fully overwritten.
+ * Requires L % B == 0.  bf16 kernels cover d in {64, 128}, B in {64, 128};
+ * fp32 kernels cover d <= 128, B <= 256.
+ */
+xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
+                                  const void* V, int32_t B, const int32_t* idx,
+                                  const int32_t* counts, void* O, void* stream);
+
+/*
+ * Dense attention softmax(Q K^T / sqrt(d)) V (causal if shape->causal): the
+ * exact attention the sparse path is measured against.  bf16 kernels need
+ * L % 64 == 0 and d in {64, 128}; fp32 kernels cover d <= 128.
+ */
+xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K,
+                        const void* V, void* O, void* stream);
+
+const char* xattn_status_str(xattn_status status);
+const char* xattn_last_error(void);
+int32_t xattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

@@ -1,0 +1,116 @@
+"""The C-ABI library loads without a GPU, exports every entry point that
+include/xattn.h declares, and rejects malformed arguments before any HIP
+call (so these checks run on the CPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_long_stride_amd.xattn as X
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "xattn.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xattn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(X.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = X.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.xattn_version() == 1
+
+
+def _shape(**kw):
+    d = dict(hq=4, hkv=2, L=4096, d=128, dtype=X.XATTN_BF16, causal=1)
+    d.update(kw)
+    return X.Shape(d["hq"], d["hkv"], d["L"], d["d"], d["dtype"], d["causal"])
+
+
+DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _score(sh, S=16, B=128, ws_bytes=1 << 40):
+    lib = X.lib()
+    return lib.xattn_score(ctypes.byref(sh), DUMMY, DUMMY, S, B, DUMMY, DUMMY, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,S,B,status", [
+    (dict(hq=3, hkv=2), 16, 128, X.XATTN_EINVAL),          # hq % hkv
+    (dict(L=4000), 16, 128, X.XATTN_EINVAL),               # L % B
+    (dict(), 24, 128, X.XATTN_EINVAL),                     # B % S
+    (dict(dtype=7), 16, 128, X.XATTN_EINVAL),
+    (dict(causal=2), 16, 128, X.XATTN_EINVAL),
+    (dict(L=0), 16, 128, X.XATTN_EINVAL),
+    (dict(), 0, 128, X.XATTN_EINVAL),
+    (dict(d=96), 16, 128, X.XATTN_EUNSUPPORTED),           # bf16 d
+    (dict(), 2, 128, X.XATTN_EUNSUPPORTED),                # B/S = 64
+    (dict(), 16, 32, X.XATTN_EUNSUPPORTED),                # B/S = 2
+])
+def test_score_rejects(kw, S, B, status):
+    assert _score(_shape(**kw), S, B) == status
+    assert X.lib().xattn_last_error()
+
+
+def test_score_workspace_checks():
+    lib = X.lib()
+    sh = _shape()
+    need = lib.xattn_score_workspace_bytes(ctypes.byref(sh), 16, 128)
+    Lr, NB = 4096 // 16, 4096 // 128
+    assert need == 4 * (sh.hq * (Lr // 32) * NB * 32 + 2 * sh.hq * (Lr // 32) * ((Lr + 63) // 64) * 32)
+    assert _score(sh, ws_bytes=need - 1) == X.XATTN_EWORKSPACE
+    assert lib.xattn_score(ctypes.byref(sh), DUMMY, DUMMY, 16, 128, DUMMY, None, need, None) == X.XATTN_EINVAL
+    assert lib.xattn_score(ctypes.byref(sh), None, DUMMY, 16, 128, DUMMY, DUMMY, need, None) == X.XATTN_EINVAL
+    assert lib.xattn_score_workspace_bytes(ctypes.byref(_shape(hq=3)), 16, 128) == 0
+    fp32 = _shape(dtype=X.XATTN_FP32)
+    assert lib.xattn_score_workspace_bytes(ctypes.byref(fp32), 16, 128) == 0
+
+
+def test_select_rejects():
+    lib = X.lib()
+
+    def call(hq=2, NB=8, causal=1, tau=(0.9, 0.9), null=False):
+        t = np.asarray(tau, dtype=np.float32)
+        return lib.xattn_select(hq, NB, causal, DUMMY, t.ctypes.data_as(ctypes.c_void_p),
+                                None if null else DUMMY, DUMMY, DUMMY, None)
+
+    assert call(tau=(0.9, 0.0)) == X.XATTN_EINVAL
+    assert call(tau=(1.5, 0.9)) == X.XATTN_EINVAL
+    assert call(tau=(float("nan"), 0.9)) == X.XATTN_EINVAL
+    assert call(NB=0) == X.XATTN_EINVAL
+    assert call(causal=3) == X.XATTN_EINVAL
+    assert call(null=True) == X.XATTN_EINVAL
+    assert call(NB=4097) == X.XATTN_EUNSUPPORTED
+    assert call(hq=129, tau=np.full(129, 0.9)) == X.XATTN_EUNSUPPORTED
+
+
+def test_attention_rejects():
+    lib = X.lib()
+    sh = _shape()
+    assert lib.xattn_sparse_prefill(ctypes.byref(sh), DUMMY, DUMMY, DUMMY, 256, DUMMY, DUMMY, DUMMY,
+                                    None) == X.XATTN_EUNSUPPORTED
+    assert lib.xattn_sparse_prefill(ctypes.byref(sh), DUMMY, DUMMY, DUMMY, 100, DUMMY, DUMMY, DUMMY,
+                                    None) == X.XATTN_EINVAL
+    assert lib.xattn_sparse_prefill(ctypes.byref(sh), DUMMY, DUMMY, DUMMY, 128, None, DUMMY, DUMMY,
+                                    None) == X.XATTN_EINVAL
+    assert lib.xattn_full(ctypes.byref(_shape(L=4000)), DUMMY, DUMMY, DUMMY, DUMMY,
+                          None) == X.XATTN_EUNSUPPORTED
+    assert lib.xattn_full(ctypes.byref(_shape(d=80)), DUMMY, DUMMY, DUMMY, DUMMY,
+                          None) == X.XATTN_EUNSUPPORTED
+    assert lib.xattn_full(None, DUMMY, DUMMY, DUMMY, DUMMY, None) == X.XATTN_EINVAL
+
+
+def test_status_strings():
+    lib = X.lib()
+    for s in range(5):
+        assert lib.xattn_status_str(s)

@@ -1,0 +1,182 @@
+"""GPU parity at the full sizes of configs 1-5, in the launch configuration
+the bench times, on sampled query blocks the oracle computes one by one.
+
+For each config: the whole path runs on the GPU (score -> select -> sparse
+prefill, and dense attention); a seeded sample of (head, query block) rows,
+always including the first and last query block, is checked against the
+oracle: scores, masks (with tau-band / tie-band counts), the selection on the
+oracle's own fp32 scores, sparse output on the oracle's selection, and dense
+output."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle as O
+from parity import (assert_outputs_close, assert_scores_close, classify_rows, gpu_selected,
+                    mask_bits, out_to_f64, to_device)
+from workloads import generate, get_config
+
+pytestmark = pytest.mark.gpu
+
+SAMPLES = {1: 32, 2: 12, 3: 10, 4: 6, 5: 10}
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _samples(cfg, n):
+    rng = np.random.default_rng(1234 + cfg.cid)
+    hs = rng.integers(0, cfg.hq, size=n)
+    qbs = rng.integers(0, cfg.nb, size=n)
+    pairs = {(int(h), int(q)) for h, q in zip(hs, qbs)}
+    pairs |= {(0, 0), (cfg.hq - 1, cfg.nb - 1), (cfg.hq // 2, cfg.nb // 2)}
+    return sorted(pairs)
+
+
+def run(cid):
+    """Generate config `cid`, run the GPU path once, keep what the tests read."""
+    import torch
+    from block_sparse_long_stride_amd import (xattn_full, xattn_score, xattn_select,
+                                              xattn_sparse_prefill)
+    cfg = get_config(cid)
+    print(f"[config {cid}] generating", flush=True)
+    w = generate(cfg)
+    dev = {k: to_device(getattr(w, k), cfg.dtype) for k in ("Q", "K", "V")}
+    print(f"[config {cid}] GPU path", flush=True)
+    scores = xattn_score(dev["Q"], dev["K"], cfg.S, cfg.B, cfg.causal)
+    mask, idx, counts = xattn_select(scores, w.tau, cfg.causal)
+    out_s = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx, counts, cfg.causal)
+    out_f = xattn_full(dev["Q"], dev["K"], dev["V"], cfg.causal)
+    _sync()
+    pairs = _samples(cfg, SAMPLES[cid])
+    res = {"pairs": pairs, "scores": {}, "mask": {}, "idx": {}, "counts": {}, "out_f": {}}
+    for h, qb in pairs:
+        res["scores"][(h, qb)] = scores[h, qb].cpu().numpy()
+        res["mask"][(h, qb)] = mask[h, qb].cpu().numpy().view(np.uint64)
+        res["idx"][(h, qb)] = idx[h, qb].cpu().numpy()
+        res["counts"][(h, qb)] = int(counts[h, qb])
+        res["out_f"][(h, qb)] = out_to_f64(out_f[h, qb * cfg.B:(qb + 1) * cfg.B])
+    c = counts.cpu().numpy().astype(np.int64)
+    valid = cfg.hq * (cfg.nb * (cfg.nb + 1) // 2 if cfg.causal else cfg.nb * cfg.nb)
+    res["density"] = float(c.sum()) / valid
+    del scores, mask, idx, counts, out_s, out_f
+    # oracle rows for the sample, one head at a time
+    ora, sels = {}, {}
+    for h in sorted({h for h, _ in pairs}):
+        qbs = [qb for hh, qb in pairs if hh == h]
+        g = h // cfg.group
+        qh, kg = w.q64(h), w.k64(g)
+        sc = O.block_scores(qh, kg, cfg.S, cfg.B, cfg.causal, qblocks=qbs)
+        for qb, row in zip(qbs, sc):
+            ora[(h, qb)] = row
+            sels[(h, qb)] = O.find_blocks(row, qb + 1 if cfg.causal else cfg.nb, float(w.tau[h]))
+    res["ora"], res["sels"] = ora, sels
+    return cfg, w, dev, res
+
+
+CIDS = [1, 2, 3, 4, 5]
+
+
+@pytest.fixture(scope="module", params=CIDS, ids=[f"config{c}" for c in CIDS])
+def fullsize(request):
+    """One config at a time: pytest groups the tests by this module-scoped
+    parameter, so each config is generated and run once."""
+    import torch
+    out = run(request.param)
+    yield out
+    del out
+    torch.cuda.empty_cache()
+
+
+def test_fullsize_scores(fullsize):
+    cfg, w, dev, r = fullsize
+    cid = cfg.cid
+    rel = 0.0
+    for key in r["pairs"]:
+        rel = max(rel, assert_scores_close(r["scores"][key], r["ora"][key], f"scores {key}"))
+    print(f"[config {cid}] sampled rows {len(r['pairs'])} max rel score err {rel:.2e} "
+          f"density {r['density']:.4f}")
+
+
+def test_fullsize_masks(fullsize):
+    cfg, w, dev, r = fullsize
+    cid = cfg.cid
+    sels, srts, gsets, taus, labs = [], [], [], [], []
+    for h, qb in r["pairs"]:
+        sel = r["sels"][(h, qb)]
+        g = gpu_selected(r["idx"][(h, qb)], r["counts"][(h, qb)])
+        assert g == mask_bits(r["mask"][(h, qb)], cfg.nb)
+        assert np.all(r["idx"][(h, qb)][len(g):] == -1)
+        sels.append(sel)
+        srts.append(r["ora"][(h, qb)][sel.order])
+        gsets.append(g)
+        taus.append(float(w.tau[h]))
+        labs.append(f"h{h} qb{qb}")
+    rep = classify_rows(sels, srts, gsets, taus, labs)
+    print(f"[config {cid}] rows {rep.rows} equal {rep.equal} tau-band {rep.tau_band} "
+          f"tie-band {rep.tie_band}")
+    assert not rep.failures, rep.failures[:5]
+
+
+def test_fullsize_select_on_oracle_scores(fullsize):
+    """The oracle's fp32 score rows, placed in an otherwise-zero score matrix,
+    go through the GPU selection; sampled rows must match exactly."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_select
+    cfg, w, dev, r = fullsize
+    cid = cfg.cid
+    s = torch.zeros((cfg.hq, cfg.nb, cfg.nb), dtype=torch.float32, device="cuda")
+    rows32 = {}
+    for key in r["pairs"]:
+        rows32[key] = r["ora"][key].astype(np.float32)
+        s[key[0], key[1]] = torch.from_numpy(rows32[key]).cuda()
+    mask, idx, counts = xattn_select(s, w.tau, cfg.causal)
+    _sync()
+    for h, qb in r["pairs"]:
+        sel = O.find_blocks(rows32[(h, qb)].astype(np.float64),
+                            qb + 1 if cfg.causal else cfg.nb, float(w.tau[h]))
+        assert int(counts[h, qb]) == sel.kstar
+        assert list(idx[h, qb, :sel.kstar].cpu().numpy()) == list(sel.selected)
+        np.testing.assert_array_equal(mask[h, qb].cpu().numpy().view(np.uint64),
+                                      O.to_mask(sel, cfg.nb))
+
+
+def test_fullsize_sparse_prefill(fullsize):
+    """Sparse prefill on the oracle's selections of the sampled rows (other
+    rows get empty lists) against oracle attention over the same blocks."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_sparse_prefill
+    cfg, w, dev, r = fullsize
+    cid = cfg.cid
+    idx = torch.full((cfg.hq, cfg.nb, cfg.nb), -1, dtype=torch.int32)
+    counts = torch.zeros((cfg.hq, cfg.nb), dtype=torch.int32)
+    for key in r["pairs"]:
+        sel = r["sels"][key].selected
+        idx[key[0], key[1], :len(sel)] = torch.from_numpy(sel.astype(np.int32))
+        counts[key[0], key[1]] = len(sel)
+    out = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx.cuda(), counts.cuda(),
+                               cfg.causal)
+    _sync()
+    got, want = [], []
+    for h, qb in r["pairs"]:
+        g = h // cfg.group
+        got.append(out_to_f64(out[h, qb * cfg.B:(qb + 1) * cfg.B]))
+        want.append(O.block_sparse_attention(w.q64(h), w.k64(g), w.v64(g), cfg.B, cfg.causal, qb,
+                                             r["sels"][(h, qb)].selected))
+    st = assert_outputs_close(np.stack(got), np.stack(want), cfg.dtype)
+    print(f"[config {cid}] sparse O {st}")
+
+
+def test_fullsize_full_attention(fullsize):
+    cfg, w, dev, r = fullsize
+    cid = cfg.cid
+    got, want = [], []
+    for h, qb in r["pairs"]:
+        g = h // cfg.group
+        got.append(r["out_f"][(h, qb)])
+        want.append(O.full_attention(w.q64(h), w.k64(g), w.v64(g), cfg.B, cfg.causal, qb))
+    st = assert_outputs_close(np.stack(got), np.stack(want), cfg.dtype)
+    print(f"[config {cid}] full O {st}")

@@ -1,0 +1,230 @@
+"""GPU parity of the HIP path (through the C-ABI) against the fp64 oracle on
+small shapes that span several kernel tiles, a ragged tail, every B/S the
+bf16 scoring kernel covers, d = 64 and 128, fp32 and bf16, causal and not.
+Every stage is compared on every row here; the full-size configs are in
+test_gpu_fullsize.py."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle as O
+from parity import (assert_outputs_close, assert_scores_close, classify_rows, gpu_selected,
+                    mask_bits, out_to_f64, to_device)
+from workloads import generate, get_config
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "c1-fp32": get_config(1),
+    "llm-S8-B128": get_config(2, hq=4, hkv=2, L=4096),
+    "llm-S16-B128-offsets": get_config(3, hq=4, hkv=1, L=8192),
+    "llm-bs4-S32": get_config(3, hq=2, hkv=2, L=4096, S=32),
+    "llm-bs32-S4": get_config(2, hq=2, hkv=1, L=4096, S=4),
+    "llm-d64-B64": get_config(2, hq=2, hkv=1, L=2048, d=64, B=64, S=8),
+    "llm-d64-tau-range": get_config(4, hq=4, hkv=2, L=4096, d=64),
+    "video-ragged": get_config(5, hq=2, hkv=2, frames=3),
+    "noncausal-llm-fp32": get_config(1, causal=False, L=1024),
+}
+
+
+@functools.lru_cache(maxsize=None)
+def case(name):
+    cfg = SMALL[name]
+    w = generate(cfg)
+    dev = {k: to_device(getattr(w, k), cfg.dtype) for k in ("Q", "K", "V")}
+    scores = []
+    for h in range(cfg.hq):
+        g = h // cfg.group
+        scores.append(O.block_scores(w.q64(h), w.k64(g), cfg.S, cfg.B, cfg.causal))
+    return cfg, w, dev, np.stack(scores)
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _gpu_scores(cfg, dev):
+    from block_sparse_long_stride_amd import xattn_score
+    s = xattn_score(dev["Q"], dev["K"], cfg.S, cfg.B, cfg.causal)
+    _sync()
+    return s
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_scores_match_oracle(name):
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] score", flush=True)
+    gpu = _gpu_scores(cfg, dev).cpu().numpy()
+    rel = assert_scores_close(gpu, ora)
+    print(f"[{name}] max rel score err {rel:.2e}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_select_matches_oracle_on_same_scores(name):
+    """Both sides rank the same fp32 scores: masks, idx and counts are exact."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_select
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] select", flush=True)
+    s32 = ora.astype(np.float32)
+    mask, idx, counts = xattn_select(torch.from_numpy(s32).cuda(), w.tau, cfg.causal)
+    _sync()
+    mask, idx, counts = mask.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    NB = cfg.nb
+    for h in range(cfg.hq):
+        for qb in range(NB):
+            sel = O.find_blocks(s32[h, qb].astype(np.float64), qb + 1 if cfg.causal else NB,
+                                float(w.tau[h]))
+            assert counts[h, qb] == sel.kstar, (h, qb)
+            assert list(idx[h, qb, :sel.kstar]) == list(sel.selected), (h, qb)
+            assert np.all(idx[h, qb, sel.kstar:] == -1), (h, qb)
+            np.testing.assert_array_equal(mask[h, qb].view(np.uint64), O.to_mask(sel, NB))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_pipeline_masks_match_oracle(name):
+    """GPU score -> GPU select against the oracle's fp64 path, with band counts."""
+    from block_sparse_long_stride_amd import xattn_select
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] pipeline masks", flush=True)
+    scores = _gpu_scores(cfg, dev)
+    mask, idx, counts = xattn_select(scores, w.tau, cfg.causal)
+    _sync()
+    mask, idx, counts = mask.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+    sels, srts, gsets, taus, labs = [], [], [], [], []
+    for h in range(cfg.hq):
+        for qb in range(cfg.nb):
+            sel = O.find_blocks(ora[h, qb], qb + 1 if cfg.causal else cfg.nb, float(w.tau[h]))
+            sels.append(sel)
+            srts.append(ora[h, qb][sel.order])
+            g = gpu_selected(idx[h, qb], int(counts[h, qb]))
+            assert g == mask_bits(mask[h, qb].view(np.uint64), cfg.nb)
+            gsets.append(g)
+            taus.append(float(w.tau[h]))
+            labs.append(f"h{h} qb{qb}")
+    rep = classify_rows(sels, srts, gsets, taus, labs)
+    print(f"[{name}] rows {rep.rows} equal {rep.equal} tau-band {rep.tau_band} "
+          f"tie-band {rep.tie_band} density "
+          f"{sum(len(g) for g in gsets) / sum(s.n_valid for s in sels):.4f}")
+    assert not rep.failures, rep.failures[:5]
+
+
+def _oracle_selections(cfg, w, ora):
+    return [[O.find_blocks(ora[h, qb], qb + 1 if cfg.causal else cfg.nb, float(w.tau[h]))
+             for qb in range(cfg.nb)] for h in range(cfg.hq)]
+
+
+def _idx_tensors(cfg, sels):
+    import torch
+    idx = np.full((cfg.hq, cfg.nb, cfg.nb), -1, dtype=np.int32)
+    counts = np.zeros((cfg.hq, cfg.nb), dtype=np.int32)
+    for h in range(cfg.hq):
+        for qb in range(cfg.nb):
+            s = sels[h][qb].selected
+            idx[h, qb, :len(s)] = s
+            counts[h, qb] = len(s)
+    return torch.from_numpy(idx).cuda(), torch.from_numpy(counts).cuda()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_sparse_prefill_matches_oracle(name):
+    from block_sparse_long_stride_amd import xattn_sparse_prefill
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] sparse prefill", flush=True)
+    sels = _oracle_selections(cfg, w, ora)
+    idx, counts = _idx_tensors(cfg, sels)
+    out = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx, counts, cfg.causal)
+    _sync()
+    got = out_to_f64(out)
+    want = np.zeros_like(got)
+    for h in range(cfg.hq):
+        g = h // cfg.group
+        q, k, v = w.q64(h), w.k64(g), w.v64(g)
+        for qb in range(cfg.nb):
+            want[h, qb * cfg.B:(qb + 1) * cfg.B] = O.block_sparse_attention(
+                q, k, v, cfg.B, cfg.causal, qb, sels[h][qb].selected)
+    st = assert_outputs_close(got, want, cfg.dtype)
+    print(f"[{name}] sparse O {st}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_full_matches_oracle(name):
+    from block_sparse_long_stride_amd import xattn_full
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] full", flush=True)
+    out = xattn_full(dev["Q"], dev["K"], dev["V"], cfg.causal)
+    _sync()
+    got = out_to_f64(out)
+    want = np.zeros_like(got)
+    for h in range(cfg.hq):
+        g = h // cfg.group
+        q, k, v = w.q64(h), w.k64(g), w.v64(g)
+        for qb in range(cfg.nb):
+            want[h, qb * cfg.B:(qb + 1) * cfg.B] = O.full_attention(q, k, v, cfg.B, cfg.causal, qb)
+    st = assert_outputs_close(got, want, cfg.dtype)
+    print(f"[{name}] full O {st}")
+
+
+@pytest.mark.parametrize("name", ["c1-fp32", "llm-S8-B128", "video-ragged"])
+def test_tau_one_selects_every_block_and_matches_full(name):
+    import torch
+    from block_sparse_long_stride_amd import xattn_full, xattn_select, xattn_sparse_prefill
+    cfg, w, dev, ora = case(name)
+    scores = _gpu_scores(cfg, dev)
+    mask, idx, counts = xattn_select(scores, np.ones(cfg.hq, np.float32), cfg.causal)
+    out_s = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx, counts, cfg.causal)
+    out_f = xattn_full(dev["Q"], dev["K"], dev["V"], cfg.causal)
+    _sync()
+    c = counts.cpu().numpy()
+    want = (np.arange(cfg.nb) + 1) if cfg.causal else np.full(cfg.nb, cfg.nb)
+    assert np.all(c == want[None, :])
+    # same blocks, same kernels: identical up to the order of key blocks (ascending in both)
+    np.testing.assert_array_equal(out_to_f64(out_s), out_to_f64(out_f))
+
+
+@pytest.mark.parametrize("name", ["llm-S8-B128", "c1-fp32"])
+def test_sparse_prefill_edge_lists(name):
+    """Empty lists give zeros; invalid entries (-1, >= NB, > qb when causal)
+    are ignored; a single block equals attention over that block alone."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_sparse_prefill
+    cfg, w, dev, ora = case(name)
+    NB = cfg.nb
+    idx = np.full((cfg.hq, NB, NB), -1, dtype=np.int32)
+    counts = np.zeros((cfg.hq, NB), dtype=np.int32)
+    rng = np.random.default_rng(0)
+    expect_lists = {}
+    for h in range(cfg.hq):
+        for qb in range(NB):
+            mode = (h * NB + qb) % 4
+            if mode == 0:
+                lst, cnt = [], 0
+            elif mode == 1:
+                kb = int(rng.integers(0, qb + 1))
+                lst, cnt = [kb], 1
+            elif mode == 2:   # junk entries mixed in
+                kb = int(rng.integers(0, qb + 1))
+                lst = [-5, kb, NB + 3, min(qb + 1, NB - 1) if qb + 1 < NB else -1]
+                cnt = len(lst)
+            else:             # count larger than NB is clamped; entries after are -1
+                lst, cnt = [qb], NB + 7
+            idx[h, qb, :len(lst)] = lst
+            counts[h, qb] = cnt
+            valid = [k for k in lst[:min(cnt, NB)] if 0 <= k < NB and (not cfg.causal or k <= qb)]
+            expect_lists[(h, qb)] = valid
+    out = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, torch.from_numpy(idx).cuda(),
+                               torch.from_numpy(counts).cuda(), cfg.causal)
+    _sync()
+    got = out_to_f64(out)
+    want = np.zeros_like(got)
+    for h in range(cfg.hq):
+        g = h // cfg.group
+        q, k, v = w.q64(h), w.k64(g), w.v64(g)
+        for qb in range(NB):
+            want[h, qb * cfg.B:(qb + 1) * cfg.B] = O.block_sparse_attention(
+                q, k, v, cfg.B, cfg.causal, qb, expect_lists[(h, qb)])
+    assert_outputs_close(got, want, cfg.dtype)
