@@ -1,0 +1,247 @@
+"""Benchmark of the XAttention prefill path on one MI355X.
+
+One step = xattn_score + xattn_select + xattn_sparse_prefill over the whole
+L=131072, 32 query / 8 KV head, d=128, bf16, causal layer (S=16, B=128,
+tau=0.95), inputs already resident in HBM.  `value` is dense-equivalent
+TFLOP/s: the FLOPs of exact causal attention over the layer (4*d*hq*L(L+1)/2)
+divided by the measured time per step.
+
+Prints one JSON line.  Per-call times come from HIP events recorded on the
+stream the library launches on; the roofline object is for the dominant
+kernel (sparse prefill), priced by its algorithmic FLOPs (4*d per selected
+causal query-key pair) against the bf16 dense MFMA peak.  The CPU baseline
+times the fp64 oracle on a bounded sample of (head, query block) rows of the
+same workload and scales it to the full layer.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full", action="store_true", help="skip timing xattn_full")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_long_stride_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(rec.get("sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, w, seconds):
+    """Time the oracle (score rows, find_blocks, block-sparse attention) on a
+    random sample of (head, query block) rows until `seconds` have elapsed,
+    then scale to all hq * NB rows."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(7)
+    heads = sorted(int(h) for h in rng.choice(cfg.hq, size=min(2, cfg.hq), replace=False))
+    per_head = {}
+    for h in heads:   # exact fp64 copies of the inputs (input preparation, not timed)
+        g = h // cfg.group
+        per_head[h] = (w.q64(h), w.k64(g), w.v64(g))
+    spent, rows = 0.0, 0
+    while spent < seconds:
+        h = heads[rows % len(heads)]
+        qb = int(rng.integers(0, cfg.nb))
+        q, k, v = per_head[h]
+        t0 = time.perf_counter()
+        sc = O.block_scores(q, k, cfg.S, cfg.B, cfg.causal, qblocks=[qb])
+        sel = O.find_blocks(sc[0], qb + 1 if cfg.causal else cfg.nb, float(w.tau[h]))
+        O.block_sparse_attention(q, k, v, cfg.B, cfg.causal, qb, sel.selected)
+        spent += time.perf_counter() - t0
+        rows += 1
+    ms_full = spent / rows * cfg.hq * cfg.nb * 1e3
+    return ms_full, rows, threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_sparse_long_stride_amd import xattn
+    from workloads import generate, get_config
+
+    cfg = get_config(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    xattn.lib()
+    t0 = time.perf_counter()
+    w = generate(cfg)
+    print(f"# generated config {cfg.cid} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    Q, K, V = up(w.Q), up(w.K), up(w.V)
+    hq, NB, L, d = cfg.hq, cfg.nb, cfg.L, cfg.d
+    sh = xattn.shape_of(Q, K, cfg.causal)
+    ws = torch.empty(xattn.xattn_score_workspace_bytes(sh, cfg.S, cfg.B), dtype=torch.uint8, device=dev)
+    scores = torch.empty((hq, NB, NB), dtype=torch.float32, device=dev)
+    mask = torch.empty((hq, NB, (NB + 63) // 64), dtype=torch.int64, device=dev)
+    idx = torch.empty((hq, NB, NB), dtype=torch.int32, device=dev)
+    counts = torch.empty((hq, NB), dtype=torch.int32, device=dev)
+    out = torch.empty_like(Q)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores, workspace=ws, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        xattn.xattn_sparse_prefill(Q, K, V, cfg.B, idx, counts, cfg.causal, out=out, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])
+    score_ms, select_ms, sparse_ms = [float(np.median(per[:, j])) for j in range(3)]
+    ev_step_ms = float(np.median(per.sum(axis=1)))
+
+    # algorithmic work
+    F_full = 4.0 * d * hq * (L * (L + 1) / 2 if cfg.causal else float(L) * L)
+    Lr = L // cfg.S
+    F_score = 2.0 * cfg.S * d * hq * (Lr * (Lr + 1) / 2 if cfg.causal else float(Lr) * Lr)
+    c = counts.to(torch.int64)
+    n_sel = int(c.sum())
+    valid = hq * (NB * (NB + 1) // 2 if cfg.causal else NB * NB)
+    if cfg.causal:
+        diag = int(((mask[:, torch.arange(NB, device=dev), torch.arange(NB, device=dev) // 64]
+                     >> (torch.arange(NB, device=dev) % 64)) & 1).sum())
+        pairs = (n_sel - diag) * cfg.B * cfg.B + diag * cfg.B * (cfg.B + 1) / 2
+    else:
+        pairs = float(n_sel) * cfg.B * cfg.B
+    F_sparse = 4.0 * d * pairs
+    # select: 4 B per valid score read + mask + idx (counts entries + -1 padding) + counts
+    sel_bytes = 4.0 * valid + mask.numel() * 8 + 4.0 * hq * NB * NB + 4.0 * hq * NB
+
+    full_ms = None
+    if not args.no_full:
+        ef = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        xattn.xattn_full(Q, K, V, cfg.causal, out=out, stream=stream)
+        ef[0].record(stream)
+        xattn.xattn_full(Q, K, V, cfg.causal, out=out, stream=stream)
+        ef[1].record(stream)
+        torch.cuda.synchronize()
+        full_ms = ef[0].elapsed_time(ef[1])
+
+    tflops = F_full / (wall_ms * 1e-3) / 1e12
+    achieved = F_sparse / (sparse_ms * 1e-3) / 1e12
+    res = {
+        "metric": "score+select+sparse-prefill ms and dense-equiv TFLOP/s at L=128K, 32/8 heads",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded RoPE'd Gaussians + shared c + sink columns; no dataset)",
+        "config": {"workload": f"config{cfg.cid} {cfg.name}: L={L}, hq={hq}, hkv={cfg.hkv}, d={d}, "
+                               f"{cfg.dtype}, {'causal' if cfg.causal else 'non-causal'}, S={cfg.S}, "
+                               f"B={cfg.B}, tau={cfg.tau if cfg.tau is not None else list(cfg.tau_range)}",
+                   "L": L, "hq": hq, "hkv": cfg.hkv, "d": d, "S": cfg.S, "B": cfg.B,
+                   "parallelism": "single GPU"},
+        "ms": {"score": round(score_ms, 3), "select": round(select_ms, 3),
+               "sparse_prefill": round(sparse_ms, 3), "events_step": round(ev_step_ms, 3),
+               "full": None if full_ms is None else round(full_ms, 3)},
+        "density": round(n_sel / valid, 5),
+        "speedup_vs_full": None if full_ms is None else round(full_ms / wall_ms, 3),
+        "kernels": {
+            "score": {"tflops": round(F_score / (score_ms * 1e-3) / 1e12, 1),
+                      "frac_bf16_peak": round(F_score / (score_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "flops": F_score},
+            "select": {"gbs": round(sel_bytes / (select_ms * 1e-3) / 1e9, 1),
+                       "frac_hbm_peak": round(sel_bytes / (select_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                       "bytes": sel_bytes},
+            "sparse_prefill": {"tflops": round(achieved, 1),
+                               "frac_bf16_peak": round(achieved / PEAK_BF16_TFLOPS, 4),
+                               "flops": F_sparse},
+            "full": None if full_ms is None else {
+                "tflops": round(F_full / (full_ms * 1e-3) / 1e12, 1),
+                "frac_bf16_peak": round(F_full / (full_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        },
+        "roofline": {"bound": "mfma", "kernel": "flash_bf16_kernel (xattn_sparse_prefill)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic("flash_bf16", f"config{cfg.cid}")},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        ms_cpu, rows, threads = cpu_baseline(cfg, w, args.cpu_sample_seconds)
+        res["cpu_baseline"] = {"value": round(F_full / (ms_cpu * 1e-3) / 1e12, 6),
+                               "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
+                               "kind": "oracle", "ms_per_step": round(ms_cpu, 1),
+                               "sample": f"{rows} random (head, query block) rows of the same "
+                                         f"workload through oracle score, find_blocks and "
+                                         f"block-sparse attention (fp64 numpy), scaled to "
+                                         f"{hq * NB} rows"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

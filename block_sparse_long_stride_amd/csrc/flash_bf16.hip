@@ -3,24 +3,32 @@
 // section 1 step 3: attention computed on the selected blocks only).
 //
 // One workgroup per (query head, query block of B rows); each of its B/32
-// waves owns 32 query rows.  Key/value blocks -- the selected ones in sparse
-// mode, all causal-visible ones in dense mode -- stream through LDS in tiles
-// of 64 keys: K row-major, V transposed with a key permutation that matches
-// the MFMA operand layout.  Per tile a wave computes S^T = K Q^T with
-// 32x32x16 bf16 MFMAs (so each lane owns one query row), applies the causal
-// mask and an online softmax in the exp2 domain, and accumulates
-// O^T += V^T P^T with P rounded to bf16.  Query head h reads key/value head
-// h / (hq / hkv).
+// waves owns 32 query rows.  The key/value blocks to visit -- the selected
+// ones in sparse mode, all causal-visible ones in dense mode -- stream
+// through LDS in tiles of 64 keys, double buffered: while a tile is being
+// used, the next one is copied global -> LDS by direct-to-LDS loads, so the
+// copy never passes through registers.  K and V tiles are stored row-major
+// with an XOR swizzle of their 16-byte chunks (conflict-free reads for both
+// access patterns below).
+//
+// Per tile a wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs (each lane
+// then owns one query row), applies the causal mask, an online softmax in the
+// exp2 domain (the O rescale is skipped when no row's max moved), rounds P to
+// bf16, and accumulates O^T += V^T P^T.  The V^T operand comes from the
+// row-major V tile through LDS transpose reads (ds_read_b64_tr_b16).  Query
+// head h reads key/value head h / (hq / hkv).
 #include "common.h"
 #include "launch.h"
 
 namespace xattn {
 namespace {
 
-constexpr int kKT = 64;           // keys per LDS tile
-constexpr int kKPad = 8;
-constexpr int kVPad = 8;
-constexpr int kVtRow = kKT + kVPad;
+constexpr int kKT = 64;   // keys per LDS tile
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 struct FlashParams {
   const uint16_t* Q;
@@ -34,22 +42,54 @@ struct FlashParams {
   float scale_log2;        // log2(e) / sqrt(d)
 };
 
-// Position of key k (0..63) of a tile inside a transposed V row: within each
-// group of 16 keys, bits 2 and 3 are swapped, so that the 8 keys lane-half
-// `hi` feeds to the MFMA k-slots of one 16-key step are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+// XOR swizzle of the 16-byte chunks of a tile row: chunk c of row r sits at
+// c ^ swz(r).  Reads of 8 consecutive rows at one chunk (K operand) and of 4
+// consecutive rows at two neighbouring chunks (transposed V reads) then hit
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  return (2 * (row & 7)) & (D / 8 - 1);
+}
+
+// Byte offset of element (row, col) of a swizzled [64][D] bf16 tile.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  return row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + ((col & 7) << 1);
+}
+
+// Copy one 64 x D tile (rows key0 .. key0+63 of src) into LDS by direct-to-LDS
+// loads.  Each instruction of a wave fills 1 KB of LDS in lane order; lane l
+// fetches the global chunk that the swizzled layout places at its position.
+template <int D, int NWAVES>
+__device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t* lds, int wave,
+                                          int lane) {
+  constexpr int kChunksPerRow = D / 8;
+  constexpr int kRowsPerInst = 64 / kChunksPerRow;
+  constexpr int kInsts = kKT / kRowsPerInst;   // 1 KB instructions per tile
+#pragma unroll
+  for (int n = wave; n < kInsts; n += NWAVES) {
+    const int p = n * 64 + lane;                   // 16-byte chunk position in the tile
+    const int row = p / kChunksPerRow;
+    const int c = (p % kChunksPerRow) ^ swz<D>(row);
+    const uint16_t* g = src + (size_t)(key0 + row) * D + c * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g,
+                                     (__attribute__((address_space(3))) void*)(lds + n * 1024),
+                                     16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2) void flash_bf16_kernel(FlashParams p) {
-  constexpr int kThreads = BQ * 2;
-  constexpr int kKRow = D + kKPad;
+__global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
+  constexpr int kWaves = BQ / 32;
   constexpr int kTilesPerBlock = BQ / kKT;
-  constexpr int kChunks = kKT * D / 8;                 // 16-byte chunks per K (or V) tile
-  constexpr int kPerThread = kChunks / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kKT * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * kVtRow];
+  constexpr int kTileBytes = kKT * D * 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][kTileBytes];   // [buf][K,V]
 
   const int w = xcd_swizzle(blockIdx.x, p.grid);
   if (w >= p.nwork) return;
@@ -98,107 +138,103 @@ __global__ __launch_bounds__(BQ * 2) void flash_bf16_kernel(FlashParams p) {
   float m = -INFINITY;   // running max (log2 units) of this lane's query row
   float lsum = 0.f;      // this lane's share of the running denominator
 
-  u32x4_t rk[kPerThread], rv[kPerThread];
-  auto prefetch = [&](int key0) {
-#pragma unroll
-    for (int c = 0; c < kPerThread; ++c) {
-      const int ch = tid + c * kThreads;
-      const int key = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      const size_t off = (size_t)(key0 + key) * D + col;
-      rk[c] = *(const u32x4_t*)(Kg + off);
-      rv[c] = *(const u32x4_t*)(Vg + off);
-    }
-  };
+  // per-lane pieces of the LDS addresses
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int v_row = 4 * hi + (i16 >> 2);                    // + 16u + 8r
+  const int v_col = 16 * (g16 & 1) + 4 * (i16 & 3);          // + 32dt
 
-  int key0_next = ntiles > 0 ? tile_key0(0) : -1;
-  if (key0_next >= 0) prefetch(key0_next);
+  int key0 = ntiles > 0 ? tile_key0(0) : -1;
+  if (key0 >= 0) {
+    load_tile<D, kWaves>(Kg, key0, smem[0][0], wave, lane);
+    load_tile<D, kWaves>(Vg, key0, smem[0][1], wave, lane);
+  }
+  wait_vmem();
+  __syncthreads();
+
   for (int n = 0; n < ntiles; ++n) {
-    const int key0 = key0_next;
-    __syncthreads();
-    if (key0 >= 0) {
+    const int buf = n & 1;
+    const int key0_next = (n + 1 < ntiles) ? tile_key0(n + 1) : -1;
+    if (key0_next >= 0) {
+      load_tile<D, kWaves>(Kg, key0_next, smem[buf ^ 1][0], wave, lane);
+      load_tile<D, kWaves>(Vg, key0_next, smem[buf ^ 1][1], wave, lane);
+    }
+    if (key0 >= 0 && !(p.causal && key0 > qwave0 + 31)) {
+      const uint8_t* sK = smem[buf][0];
+      const uint8_t* sV = smem[buf][1];
+      // S^T (64 keys x 32 queries) as two 32x32 tiles
+      f32x16_t s[2];
 #pragma unroll
-      for (int c = 0; c < kPerThread; ++c) {
-        const int ch = tid + c * kThreads;
-        const int key = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *(u32x4_t*)&sK[key * kKRow + col] = rk[c];
-        const int pos = vt_pos(key);
+      for (int i = 0; i < 2; ++i) {
+        s[i] = f32x16_t{};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t two = rv[c][e];
-          sVt[(col + 2 * e) * kVtRow + pos] = (uint16_t)(two & 0xFFFFu);
-          sVt[(col + 2 * e + 1) * kVtRow + pos] = (uint16_t)(two >> 16);
+        for (int t = 0; t < D / 16; ++t) {
+          const bf16x8_t kf =
+              as_bf16x8(*(const u32x4_t*)(sK + tile_off<D>(i * 32 + l32, 16 * t + 8 * hi)));
+          s[i] = mfma_32x32x16(kf, qf[t], s[i]);
         }
       }
-    }
-    __syncthreads();
-    if (n + 1 < ntiles) {
-      key0_next = tile_key0(n + 1);
-      if (key0_next >= 0) prefetch(key0_next);
-    }
-    if (key0 < 0) continue;
-    if (p.causal && key0 > qwave0 + 31) continue;   // whole tile right of this wave's rows
-
-    // S^T (64 keys x 32 queries) as two 32x32 tiles
-    f32x16_t s[2];
+      if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      s[i] = f32x16_t{};
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)&sK[(i * 32 + l32) * kKRow + 16 * t + 8 * hi]);
-        s[i] = mfma_32x32x16(kf, qf[t], s[i]);
+          for (int v = 0; v < 16; ++v) {
+            const int key = key0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
+            if (key > qrow) s[i][v] = -INFINITY;
+          }
       }
-    }
-    // scale, mask, running max
-    const bool diag = p.causal && (key0 + kKT - 1 > qwave0);
-    float mloc = -INFINITY;
+      float mloc = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float z = s[i][v] * p.scale_log2;
-        if (diag) {
-          const int key = key0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-          if (key > qrow) z = -INFINITY;
-        }
-        s[i][v] = z;
-        mloc = fmaxf(mloc, z);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // No branch on per-row values: MFMAs below must run with the whole wave.
-    // A row with nothing visible yet keeps m = -inf and gets p = 0, alpha = 0.
-    const float mnew = fmaxf(m, mloc);
-    const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - mref);  // m == -inf gives 0
-    m = mnew;
-    float rs = 0.f;
-    bf16x8_t pf[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = u >> 1, v0 = (u & 1) * 8;
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float z0 = s[i][v0 + 2 * e], z1 = s[i][v0 + 2 * e + 1];
-        const float p0 = fast_exp2(z0 - mref), p1 = fast_exp2(z1 - mref);
-        rs += p0 + p1;
-        pk[e] = pack_bf16x2(p0, p1);
-      }
-      pf[u] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-    }
-    lsum = lsum * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      o[dt] *= alpha;
+        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      // No branch on per-row values around MFMAs: a row with nothing visible
+      // yet keeps m = -inf and gets p = 0 and alpha = 0.
+      const float mnew = fmaxf(m, mloc * p.scale_log2);
+      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = fast_exp2(m - mref);   // m == -inf gives 0
+      m = mnew;
+      float rs = 0.f;
+      bf16x8_t pf[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8_t vf = as_bf16x8(*(const u32x4_t*)&sVt[(dt * 32 + l32) * kVtRow + 16 * u + 8 * hi]);
-        o[dt] = mfma_32x32x16(vf, pf[u], o[dt]);
+        const int i = u >> 1, v0 = (u & 1) * 8;
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], p.scale_log2, -mref));
+          const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], p.scale_log2, -mref));
+          rs += p0 + p1;
+          pk[e] = cvt2_bf16(p0, p1);
+        }
+        pf[u] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+      }
+      lsum = lsum * alpha + rs;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r0 = 16 * u + v_row, c0 = 32 * dt + v_col;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(sV + tile_off<D>(r0, c0)));
+          const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(sV + tile_off<D>(r0 + 8, c0)));
+          const u32x4_t vv = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                              __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]};
+          o[dt] = mfma_32x32x16(as_bf16x8(vv), pf[u], o[dt]);
+        }
       }
     }
+    key0 = key0_next;
+    wait_vmem();
+    __syncthreads();
   }
 
-  // normalise and store: lane holds O[qrow][32 dt + 8 g + 4 hi + r]
+  // normalise and store: lane holds O[qrow][32 dt + 8 gg + 4 hi + r]
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
   uint16_t* op = p.O + ((size_t)h * p.L + qrow) * D;
@@ -208,8 +244,8 @@ __global__ __launch_bounds__(BQ * 2) void flash_bf16_kernel(FlashParams p) {
     for (int gg = 0; gg < 4; ++gg) {
       const int col = dt * 32 + 8 * gg + 4 * hi;
       u32x2_t v;
-      v[0] = pack_bf16x2(o[dt][4 * gg] * inv, o[dt][4 * gg + 1] * inv);
-      v[1] = pack_bf16x2(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
+      v[0] = cvt2_bf16(o[dt][4 * gg] * inv, o[dt][4 * gg + 1] * inv);
+      v[1] = cvt2_bf16(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
       *(u32x2_t*)(op + col) = v;
     }
 }
