@@ -43,12 +43,17 @@ struct FlashParams {
 };
 
 // XOR swizzle of the 16-byte chunks of a tile row: chunk c of row r sits at
-// c ^ swz(r).  Reads of 8 consecutive rows at one chunk (K operand) and of 4
-// consecutive rows at two neighbouring chunks (transposed V reads) then hit
-// distinct banks.
+// c ^ swz(r).  gfx950's LDS behaves as 64 four-byte banks (256 bytes per bank
+// line), so the bank group of a chunk is its byte offset / 16 mod 16.  For
+// d = 128 (one row per bank line) swz(r) = 4(r mod 4) + (r/4 mod 4) makes both
+// access patterns conflict-free: K-operand reads (consecutive rows, one chunk
+// each) and transposed V reads (4 consecutive rows x 4 neighbouring chunks per
+// 32 lanes).  For d = 64 two rows share a bank line and swz(r) =
+// 4(r/2 mod 2) + 2(r/4 mod 2) keeps the transposed reads conflict-free.
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  return (2 * (row & 7)) & (D / 8 - 1);
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1);
 }
 
 // Byte offset of element (row, col) of a swizzled [64][D] bf16 tile.
@@ -66,8 +71,10 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t
   constexpr int kChunksPerRow = D / 8;
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
   constexpr int kInsts = kKT / kRowsPerInst;   // 1 KB instructions per tile
+  static_assert(kInsts % NWAVES == 0, "tile instructions must split evenly over waves");
 #pragma unroll
-  for (int n = wave; n < kInsts; n += NWAVES) {
+  for (int k = 0; k < kInsts / NWAVES; ++k) {
+    const int n = k * NWAVES + wave;               // wave is uniform (scalar)
     const int p = n * 64 + lane;                   // 16-byte chunk position in the tile
     const int row = p / kChunksPerRow;
     const int c = (p % kChunksPerRow) ^ swz<D>(row);
@@ -89,17 +96,29 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   constexpr int kWaves = BQ / 32;
   constexpr int kTilesPerBlock = BQ / kKT;
   constexpr int kTileBytes = kKT * D * 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2][2][kTileBytes];   // [buf][K,V]
+  // Two K/V buffers as distinct objects: with the loop unrolled by two every
+  // access names its buffer at compile time, so the compiler can see that LDS
+  // reads of one buffer do not wait on the direct-to-LDS copy into the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
 
+  // Work order (kv group, query block descending, head within group): the
+  // XCD swizzle hands each XCD a contiguous range, so an XCD works on one KV
+  // group at a time and its L2 serves that group's K/V to all its CUs; within
+  // the group the longest causal rows start first.
   const int w = xcd_swizzle(blockIdx.x, p.grid);
   if (w >= p.nwork) return;
-  const int qb = p.NB - 1 - w / p.hq;     // longest causal rows first
-  const int h = w % p.hq;
-  const int g = h / p.group;
+  const int per_group = p.NB * p.group;
+  const int g = w / per_group;
+  const int rem = w % per_group;
+  const int qb = p.NB - 1 - rem / p.group;
+  const int h = g * p.group + rem % p.group;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const int qrow = qb * BQ + wave * 32 + l32;   // this lane's query token
   const int qwave0 = qb * BQ + wave * 32;
@@ -115,19 +134,24 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
     for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qp + 16 * t));
   }
 
+  // Sparse mode: the workgroup's block list is staged in LDS once, so the
+  // per-tile lookup is an LDS read rather than a global-memory round trip.
+  extern __shared__ int32_t s_list[];
   int nkb;
-  const int32_t* list = nullptr;
-  if (p.idx) {
+  const bool sparse = p.idx != nullptr;
+  if (sparse) {
     nkb = p.counts[(size_t)h * p.NB + qb];
     nkb = nkb < 0 ? 0 : (nkb > p.NB ? p.NB : nkb);
-    list = p.idx + ((size_t)h * p.NB + qb) * p.NB;
+    const int32_t* list = p.idx + ((size_t)h * p.NB + qb) * p.NB;
+    for (int j = tid; j < nkb; j += BQ * 2) s_list[j] = list[j];
+    __syncthreads();
   } else {
     nkb = p.causal ? qb + 1 : p.NB;
   }
   const int ntiles = nkb * kTilesPerBlock;
   auto tile_key0 = [&](int n) -> int {   // first key of tile n, or -1 to skip it
     const int j = n / kTilesPerBlock;
-    const int kb = list ? list[j] : j;
+    const int kb = sparse ? __builtin_amdgcn_readfirstlane(s_list[j]) : j;
     if (kb < 0 || kb >= p.NB || (p.causal && kb > qb)) return -1;
     return kb * BQ + (n % kTilesPerBlock) * kKT;
   };
@@ -138,29 +162,42 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   float m = -INFINITY;   // running max (log2 units) of this lane's query row
   float lsum = 0.f;      // this lane's share of the running denominator
 
-  // per-lane pieces of the LDS addresses
-  const int g16 = lane >> 4, i16 = lane & 15;
-  const int v_row = 4 * hi + (i16 >> 2);                    // + 16u + 8r
-  const int v_col = 16 * (g16 & 1) + 4 * (i16 & 3);          // + 32dt
+  // Per-lane LDS byte offsets.  The swizzle repeats every 16 rows.  K operand:
+  // row 32i + l32, chunk 2t + hi -- fixed per lane and t (the i = 1 half is
+  // 32 rows further).  V operand (transposed reads): row 16u + 8r + 4hi + i16/4
+  // and column 32dt + 16(g16 & 1) + 4(i16 & 3) -- fixed per lane, dt and r;
+  // u adds whole 16-row groups.
+  int koff[D / 16], voff[D / 32][2];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) koff[t] = tile_off<D>(l32, 16 * t + 8 * hi);
+    const int vrow = 4 * hi + (i16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        voff[dt][r] = tile_off<D>(vrow + 8 * r, 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3));
+  }
 
   int key0 = ntiles > 0 ? tile_key0(0) : -1;
   if (key0 >= 0) {
-    load_tile<D, kWaves>(Kg, key0, smem[0][0], wave, lane);
-    load_tile<D, kWaves>(Vg, key0, smem[0][1], wave, lane);
+    load_tile<D, kWaves>(Kg, key0, sK0, wave, lane);
+    load_tile<D, kWaves>(Vg, key0, sV0, wave, lane);
   }
   wait_vmem();
   __syncthreads();
 
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
+  // One tile: start copying tile n+1 into the other buffer, use tile n, then
+  // wait for the copy and synchronise.
+  auto step = [&](int n, const uint8_t* sK, const uint8_t* sV, uint8_t* nK,
+                  uint8_t* nV) __attribute__((always_inline)) {
     const int key0_next = (n + 1 < ntiles) ? tile_key0(n + 1) : -1;
     if (key0_next >= 0) {
-      load_tile<D, kWaves>(Kg, key0_next, smem[buf ^ 1][0], wave, lane);
-      load_tile<D, kWaves>(Vg, key0_next, smem[buf ^ 1][1], wave, lane);
+      load_tile<D, kWaves>(Kg, key0_next, nK, wave, lane);
+      load_tile<D, kWaves>(Vg, key0_next, nV, wave, lane);
     }
     if (key0 >= 0 && !(p.causal && key0 > qwave0 + 31)) {
-      const uint8_t* sK = smem[buf][0];
-      const uint8_t* sV = smem[buf][1];
       // S^T (64 keys x 32 queries) as two 32x32 tiles
       f32x16_t s[2];
 #pragma unroll
@@ -168,8 +205,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
         s[i] = f32x16_t{};
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          const bf16x8_t kf =
-              as_bf16x8(*(const u32x4_t*)(sK + tile_off<D>(i * 32 + l32, 16 * t + 8 * hi)));
+          const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
           s[i] = mfma_32x32x16(kf, qf[t], s[i]);
         }
       }
@@ -218,11 +254,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int r0 = 16 * u + v_row, c0 = 32 * dt + v_col;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(sV + tile_off<D>(r0, c0)));
-          const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16*)(sV + tile_off<D>(r0 + 8, c0)));
+          const uint8_t* vp = sV + 16 * u * D * 2;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][0]));
+          const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][1]));
           const u32x4_t vv = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                               __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]};
           o[dt] = mfma_32x32x16(as_bf16x8(vv), pf[u], o[dt]);
@@ -232,6 +266,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
     key0 = key0_next;
     wait_vmem();
     __syncthreads();
+  };
+  for (int n = 0; n < ntiles; n += 2) {
+    step(n, sK0, sV0, sK1, sV1);
+    if (n + 1 < ntiles) step(n + 1, sK1, sV1, sK0, sV0);
   }
 
   // normalise and store: lane holds O[qrow][32 dt + 8 gg + 4 hi + r]
@@ -252,7 +290,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
 
 template <int D, int BQ>
 hipError_t launch(const FlashParams& fp, hipStream_t st) {
-  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 2), 0, st, fp);
+  const size_t list_bytes = fp.idx ? (size_t)fp.NB * sizeof(int32_t) : 0;
+  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 2), list_bytes, st, fp);
   return hipGetLastError();
 }
 
