@@ -72,14 +72,17 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
   constexpr int kInsts = kKT / kRowsPerInst;   // 1 KB instructions per tile
   static_assert(kInsts % NWAVES == 0, "tile instructions must split evenly over waves");
+  // uniform tile base (scalar) + per-lane 32-bit byte offset: the load uses
+  // the scalar-base addressing form, no 64-bit vector address math
+  const char* tile = (const char*)(src + (size_t)key0 * D);
 #pragma unroll
   for (int k = 0; k < kInsts / NWAVES; ++k) {
     const int n = k * NWAVES + wave;               // wave is uniform (scalar)
     const int p = n * 64 + lane;                   // 16-byte chunk position in the tile
     const int row = p / kChunksPerRow;
     const int c = (p % kChunksPerRow) ^ swz<D>(row);
-    const uint16_t* g = src + (size_t)(key0 + row) * D + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g,
+    const uint32_t off = (uint32_t)(row * D * 2 + c * 16);
+    __builtin_amdgcn_global_load_lds((const void*)(tile + off),
                                      (__attribute__((address_space(3))) void*)(lds + n * 1024),
                                      16, 0, 0);
   }
@@ -198,17 +201,38 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
       load_tile<D, kWaves>(Vg, key0_next, nV, wave, lane);
     }
     if (key0 >= 0 && !(p.causal && key0 > qwave0 + 31)) {
-      // S^T (64 keys x 32 queries) as two 32x32 tiles
-      f32x16_t s[2];
+      // S^T (64 keys x 32 queries) as two 32x32 tiles.  K fragments are read
+      // kAhead k-steps before their MFMAs so LDS latency overlaps the matrix
+      // work instead of stalling each MFMA.
+      constexpr int kSteps = D / 16;
+      constexpr int kAhead = 3;
+      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+      bf16x8_t kfr[kAhead + 1][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        s[i] = f32x16_t{};
+      for (int t = 0; t < kAhead; ++t)
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const bf16x8_t kf = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
-          s[i] = mfma_32x32x16(kf, qf[t], s[i]);
+        for (int i = 0; i < 2; ++i)
+          kfr[t][i] = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
+#pragma unroll
+      for (int t = 0; t < kSteps; ++t) {
+        if (t + kAhead < kSteps) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            kfr[(t + kAhead) % (kAhead + 1)][i] =
+                as_bf16x8(*(const u32x4_t*)(sK + koff[t + kAhead] + i * 32 * D * 2));
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) s[i] = mfma_32x32x16(kfr[t % (kAhead + 1)][i], qf[t], s[i]);
       }
+      // Keep the reads kAhead steps ahead: the scheduler otherwise sinks them
+      // next to their MFMAs.  (mask 0x100: DS read, 0x008: MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+      for (int t = 0; t < kSteps - kAhead; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
       if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -223,14 +247,25 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-      // No branch on per-row values around MFMAs: a row with nothing visible
-      // yet keeps m = -inf and gets p = 0 and alpha = 0.
-      const float mnew = fmaxf(m, mloc * p.scale_log2);
-      const float mref = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(m - mref);   // m == -inf gives 0
-      m = mnew;
-      float rs = 0.f;
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;
+      // The reference max m of a row only moves when this tile's max exceeds it
+      // by more than kSlack (log2 units), so P stays <= 2^kSlack and the O /
+      // denominator rescale (a wave-uniform branch) is rare.  The result is
+      // unchanged: numerator and denominator share the reference.  A row with
+      // nothing visible yet keeps m = -inf and gets p = 0.
+      constexpr float kSlack = 8.0f;
+      if (__ballot(mloc > m + kSlack)) {
+        const float mnew = (mloc > m + kSlack) ? mloc : m;
+        const float alpha = fast_exp2(m - mnew);   // m == -inf gives 0; unchanged rows 1
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m = mnew;
+      }
+      const float mref = (m == -INFINITY) ? 0.f : m;
+      // P in bf16; the denominator sums the same rounded values (packed dot2).
+      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float rs0 = 0.f, rs1 = 0.f;
       bf16x8_t pf[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -240,16 +275,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], p.scale_log2, -mref));
           const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], p.scale_log2, -mref));
-          rs += p0 + p1;
           pk[e] = cvt2_bf16(p0, p1);
+          if (e & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ones, rs1, false);
+          else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ones, rs0, false);
         }
         pf[u] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
       }
-      lsum = lsum * alpha + rs;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-      }
+      lsum += rs0 + rs1;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
