@@ -27,11 +27,13 @@
 namespace xattn {
 namespace {
 
-constexpr int kTile = 128;       // reshaped rows / columns per workgroup tile
+constexpr int kTileC = 128;      // reshaped columns c per workgroup tile
+constexpr int kTileR = 256;      // reshaped rows R per workgroup tile
 constexpr int kWaveCols = 64;    // columns per wave (and per softmax snapshot)
-constexpr int kKC = 32;          // reduction chunk (elements of S*d)
-constexpr int kPad = 8;          // LDS row padding (elements)
-constexpr int kLdsRow = kKC + kPad;
+constexpr int kWaveRows = 128;   // rows per wave
+constexpr int kKC = 32;          // reduction chunk (elements of S*d): 64-byte LDS rows
+constexpr int kStageBytes = (kTileC + kTileR) * kKC * 2;
+constexpr int kDmaPerWave = (kTileC + kTileR) * kKC * 2 / 1024 / 4;   // 1 KB copies per wave per chunk
 
 struct GemmParams {
   const uint16_t* Q;
@@ -40,14 +42,29 @@ struct GemmParams {
   float* M;   // [hq][nR32][nct][32]
   float* Z;   // [hq][nR32][nct][32]
   int L, S, group, NB, Lr, nR32, nct;
-  int causal, nt, tiles_per_head, nwork, grid;
+  int causal, ntr, ntc, tiles_per_head, nwork, grid;
   float scale_log2;
 };
 
+// LDS rows hold one 32-element (64-byte) chunk of a reshaped row; their four
+// 16-byte pieces are XOR-swizzled by (row / 4) mod 4 so that 16 consecutive
+// rows read at the same piece fall in distinct bank groups (64 banks).
+__device__ __forceinline__ int chunk_off(int row, int piece) {
+  return row * 64 + ((piece ^ ((row >> 2) & 3)) << 4);
+}
+
+__device__ __forceinline__ void wait_vmem_dma() {
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");   // kDmaPerWave copies may stay in flight
+}
+
 template <int D, int BS>
-__global__ __launch_bounds__(256) void score_gemm(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][kTile * kLdsRow];
+__global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
+  static_assert(kDmaPerWave == 6, "wait_vmem_dma assumes six copies per wave per chunk");
+  // Three LDS stages as distinct objects (the chunk loop is unrolled by three)
+  // so LDS reads of one stage never wait on the direct-to-LDS copies into another.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
 
   const int w = xcd_swizzle(blockIdx.x, p.grid);
   if (w >= p.nwork) return;
@@ -57,16 +74,17 @@ __global__ __launch_bounds__(256) void score_gemm(GemmParams p) {
   const int g = w / (p.group * p.tiles_per_head);
   const int h = g * p.group + hh;
   int tr, tc;
-  if (p.causal) {
-    tr = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-    while (tr * (tr + 1) / 2 > t) --tr;
-    tc = t - tr * (tr + 1) / 2;
+  if (p.causal) {   // row tr holds column tiles 0 .. 2tr+1, so t = tr(tr+1) + tc
+    tr = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) <= t) ++tr;
+    while (tr * (tr + 1) > t) --tr;
+    tc = t - tr * (tr + 1);
+    if (tc >= p.ntc) return;   // clipped last row
   } else {
-    tr = t / p.nt;
-    tc = t % p.nt;
+    tr = t / p.ntc;
+    tc = t % p.ntc;
   }
-  const int R0 = tr * kTile, C0 = tc * kTile;
+  const int R0 = tr * kTileR, C0 = tc * kTileC;
   const int F = p.S * D;
   const int Lr = p.Lr;
   const uint16_t* Qh = p.Q + (size_t)h * p.L * D;
@@ -74,76 +92,110 @@ __global__ __launch_bounds__(256) void score_gemm(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wc = wave & 1, wr = wave >> 1;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // global -> register staging: 2 rows of Q and 2 rows of K' per thread
-  const int lrow = tid >> 2, lcol = (tid & 3) * 8;
-  u32x4_t rq[2], rk[2];
-  auto load_chunk = [&](int kc) {
+  // Direct-to-LDS copies through buffer resources (buffer_load ... lds).  A
+  // stage holds kTileC key rows then kTileR query rows; copy n (1 KB) fills
+  // rows 16n .. 16n+15, lane -> row 16n + lane/4 and piece lane % 4.  Each
+  // lane's byte offset is fixed for the whole K loop (no address register is
+  // rewritten while copies are in flight); the chunk only moves the scalar
+  // offset.  Rows past Lr (ragged last tile) re-read row Lr-1: finite data
+  // whose products are masked or never stored.
+  const __amdgpu_buffer_rsrc_t rsrc_k =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, p.L * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_q =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, p.L * D * 2, 0x00020000);
+  uint32_t dma_off[kDmaPerWave];
+#pragma unroll
+  for (int k = 0; k < kDmaPerWave; ++k) {
+    const int n = k * 4 + wave;
+    const int row = n * 16 + (lane >> 2);
+    const int piece = (lane & 3) ^ ((row >> 2) & 3);
+    if (k < kTileC / 64) {   // copies 0 .. kTileC/64-1 of every wave cover the key rows
+      const int C = min(C0 + row, Lr - 1);
+      dma_off[k] = (uint32_t)(C * p.S * D * 2 + piece * 16);
+    } else {
+      const int R = min(R0 + row - kTileC, Lr - 1);
+      dma_off[k] = (uint32_t)(R * F * 2 + piece * 16);
+    }
+  }
+  const int nk = F / kKC;
+  auto issue = [&](int kc, uint8_t* stage) __attribute__((always_inline)) {
+    kc = min(kc, nk - 1);   // past the end: harmless reload, keeps the copy count fixed
     const int f0 = kc * kKC;
     const int a = f0 / D, e0 = f0 % D;
+    // key operand: sub-row S-1-a of key group c (the stride reshape, reversed phase)
+    const uint32_t koff = (uint32_t)(((p.S - 1 - a) * D + e0) * 2);
+    const uint32_t qoff = (uint32_t)(f0 * 2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int R = R0 + i * 64 + lrow;
-      const int C = C0 + i * 64 + lrow;
-      rq[i] = (R < Lr) ? *(const u32x4_t*)(Qh + (size_t)R * F + f0 + lcol) : u32x4_t{0, 0, 0, 0};
-      rk[i] = (C < Lr) ? *(const u32x4_t*)(Kg + ((size_t)C * p.S + (p.S - 1 - a)) * D + e0 + lcol)
-                       : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(u32x4_t*)&sQ[buf][(i * 64 + lrow) * kLdsRow + lcol] = rq[i];
-      *(u32x4_t*)&sK[buf][(i * 64 + lrow) * kLdsRow + lcol] = rk[i];
+    for (int k = 0; k < kDmaPerWave; ++k) {
+      const int n = k * 4 + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < kTileC / 64 ? rsrc_k : rsrc_q,
+                                               (__attribute__((address_space(3))) void*)(stage + n * 1024),
+                                               16, dma_off[k], k < kTileC / 64 ? koff : qoff, 0, 0);
     }
   };
 
   // a wave whose whole column range lies right of its last row is fully masked
-  const bool wave_live = !p.causal || (C0 + wc * kWaveCols <= R0 + wr * 64 + 63);
+  const bool wave_live = !p.causal || (C0 + wc * kWaveCols <= R0 + wr * kWaveRows + kWaveRows - 1);
 
-  f32x16_t acc[2][2];
+  // fragment offsets: A = key rows 64wc + 32i + l32, B = query rows
+  // 128wr + 32j + l32; both swizzles depend on l32 only
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = chunk_off(wc * 64 + l32, 2 * ks + hi);
+    boff[ks] = kTileC * 64 + chunk_off(wr * kWaveRows + l32, 2 * ks + hi);
+  }
+
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
-  const int nk = F / kKC;
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < nk) load_chunk(kc + 1);
-    if (wave_live) {
+  auto compute = [&](const uint8_t* stage) __attribute__((always_inline)) {
 #pragma unroll
-      for (int ks = 0; ks < kKC / 16; ++ks) {
-        bf16x8_t af[2], bfr[2];
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[2], bfr[4];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = as_bf16x8(*(const u32x4_t*)&sK[buf][(wc * 64 + i * 32 + l32) * kLdsRow + ks * 16 + hi * 8]);
+      for (int i = 0; i < 2; ++i) af[i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = as_bf16x8(*(const u32x4_t*)&sQ[buf][(wr * 64 + j * 32 + l32) * kLdsRow + ks * 16 + hi * 8]);
+      for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
-      }
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
     }
-    if (kc + 1 < nk) store_chunk(buf ^ 1);
-    __syncthreads();
+  };
+  // One chunk: copy chunk kc+2 into the stage freed last chunk, multiply chunk
+  // kc, wait until chunk kc+1 has landed, synchronise.
+  auto step = [&](int kc, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
+    issue(kc + 2, nxt);
+    if (kc < nk && wave_live) compute(cur);
+    wait_vmem_dma();
+    __builtin_amdgcn_s_barrier();
+  };
+  issue(0, st0);
+  issue(1, st1);
+  wait_vmem_dma();
+  __builtin_amdgcn_s_barrier();
+  for (int kc = 0; kc < nk; kc += 3) {
+    step(kc, st0, st2);
+    step(kc + 1, st1, st0);
+    step(kc + 2, st2, st1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (!wave_live) return;
 
   // ---- epilogue: per reshaped row R (one per lane and R-tile) ---------------
   const int cw = C0 + wc * kWaveCols;   // first column of this wave's range
   const int ct = cw / kWaveCols;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int R = R0 + wr * 64 + j * 32 + l32;
+  for (int j = 0; j < 4; ++j) {
+    const int R = R0 + wr * kWaveRows + j * 32 + l32;
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -359,8 +411,9 @@ hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S
   gp.nR32 = wl.nR32;
   gp.nct = wl.nct;
   gp.causal = s.causal;
-  gp.nt = (wl.Lr + kTile - 1) / kTile;
-  gp.tiles_per_head = s.causal ? gp.nt * (gp.nt + 1) / 2 : gp.nt * gp.nt;
+  gp.ntr = (wl.Lr + kTileR - 1) / kTileR;
+  gp.ntc = (wl.Lr + kTileC - 1) / kTileC;
+  gp.tiles_per_head = s.causal ? gp.ntr * (gp.ntr + 1) : gp.ntr * gp.ntc;
   gp.nwork = gp.tiles_per_head * s.hq;
   gp.grid = (gp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
   gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
