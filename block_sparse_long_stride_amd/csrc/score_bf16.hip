@@ -27,13 +27,17 @@
 namespace xattn {
 namespace {
 
-constexpr int kTileC = 128;      // reshaped columns c per workgroup tile
+constexpr int kWavesC = 4;       // waves along c
+constexpr int kWavesR = 2;       // waves along R
+constexpr int kWaves = kWavesC * kWavesR;
+constexpr int kTileC = 64 * kWavesC;    // reshaped columns c per workgroup tile
 constexpr int kTileR = 256;      // reshaped rows R per workgroup tile
 constexpr int kWaveCols = 64;    // columns per wave (and per softmax snapshot)
 constexpr int kWaveRows = 128;   // rows per wave
 constexpr int kKC = 32;          // reduction chunk (elements of S*d): 64-byte LDS rows
 constexpr int kStageBytes = (kTileC + kTileR) * kKC * 2;
-constexpr int kDmaPerWave = (kTileC + kTileR) * kKC * 2 / 1024 / 4;   // 1 KB copies per wave per chunk
+constexpr int kDmaPerWave = (kTileC + kTileR) * kKC * 2 / 1024 / kWaves;   // 1 KB copies per wave per chunk
+constexpr int kDmaK = kTileC * kKC * 2 / 1024 / kWaves;   // of which key-row copies
 
 struct GemmParams {
   const uint16_t* Q;
@@ -54,12 +58,12 @@ __device__ __forceinline__ int chunk_off(int row, int piece) {
 }
 
 __device__ __forceinline__ void wait_vmem_dma() {
-  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");   // kDmaPerWave copies may stay in flight
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // kDmaPerWave copies may stay in flight
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
-  static_assert(kDmaPerWave == 6, "wait_vmem_dma assumes six copies per wave per chunk");
+__global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
+  static_assert(kDmaPerWave == 4, "wait_vmem_dma assumes four copies per wave per chunk");
   // Three LDS stages as distinct objects (the chunk loop is unrolled by three)
   // so LDS reads of one stage never wait on the direct-to-LDS copies into another.
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
@@ -74,12 +78,11 @@ __global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
   const int g = w / (p.group * p.tiles_per_head);
   const int h = g * p.group + hh;
   int tr, tc;
-  if (p.causal) {   // row tr holds column tiles 0 .. 2tr+1, so t = tr(tr+1) + tc
-    tr = (int)((sqrtf(4.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while ((tr + 1) * (tr + 2) <= t) ++tr;
-    while (tr * (tr + 1) > t) --tr;
-    tc = t - tr * (tr + 1);
-    if (tc >= p.ntc) return;   // clipped last row
+  if (p.causal) {   // square tiles: row tr holds column tiles 0 .. tr
+    tr = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+    while (tr * (tr + 1) / 2 > t) --tr;
+    tc = t - tr * (tr + 1) / 2;
   } else {
     tr = t / p.ntc;
     tc = t % p.ntc;
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wc = wave & 1, wr = wave >> 1;
+  const int wc = wave % kWavesC, wr = wave / kWavesC;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Direct-to-LDS copies through buffer resources (buffer_load ... lds).  A
@@ -110,10 +113,10 @@ __global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
   uint32_t dma_off[kDmaPerWave];
 #pragma unroll
   for (int k = 0; k < kDmaPerWave; ++k) {
-    const int n = k * 4 + wave;
+    const int n = k * kWaves + wave;
     const int row = n * 16 + (lane >> 2);
     const int piece = (lane & 3) ^ ((row >> 2) & 3);
-    if (k < kTileC / 64) {   // copies 0 .. kTileC/64-1 of every wave cover the key rows
+    if (k < kDmaK) {   // copies 0 .. kDmaK-1 of every wave cover the key rows
       const int C = min(C0 + row, Lr - 1);
       dma_off[k] = (uint32_t)(C * p.S * D * 2 + piece * 16);
     } else {
@@ -131,10 +134,10 @@ __global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
     const uint32_t qoff = (uint32_t)(f0 * 2);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
-      const int n = k * 4 + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < kTileC / 64 ? rsrc_k : rsrc_q,
+      const int n = k * kWaves + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < kDmaK ? rsrc_k : rsrc_q,
                                                (__attribute__((address_space(3))) void*)(stage + n * 1024),
-                                               16, dma_off[k], k < kTileC / 64 ? koff : qoff, 0, 0);
+                                               16, dma_off[k], k < kDmaK ? koff : qoff, 0, 0);
     }
   };
 
@@ -157,18 +160,24 @@ __global__ __launch_bounds__(256, 2) void score_gemm(GemmParams p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
   auto compute = [&](const uint8_t* stage) __attribute__((always_inline)) {
+    // all fragments of the chunk are read before the first MFMA, so one LDS
+    // latency is exposed per chunk instead of one per k-step
+    bf16x8_t af[2][2], bfr[2][4];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t af[2], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
+      for (int i = 0; i < 2; ++i) af[ks][i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
+      for (int j = 0; j < 4; ++j) bfr[ks][j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[i], bfr[j], acc[i][j]);
-    }
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // 12 DS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
   };
   // One chunk: copy chunk kc+2 into the stage freed last chunk, multiply chunk
   // kc, wait until chunk kc+1 has landed, synchronise.
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
 
 template <int D, int BS>
 hipError_t launch_gemm(const GemmParams& gp, hipStream_t st) {
-  hipLaunchKernelGGL((score_gemm<D, BS>), dim3(gp.grid), dim3(256), 0, st, gp);
+  hipLaunchKernelGGL((score_gemm<D, BS>), dim3(gp.grid), dim3(kWaves * 64), 0, st, gp);
   return hipGetLastError();
 }
 
@@ -413,7 +422,7 @@ hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S
   gp.causal = s.causal;
   gp.ntr = (wl.Lr + kTileR - 1) / kTileR;
   gp.ntc = (wl.Lr + kTileC - 1) / kTileC;
-  gp.tiles_per_head = s.causal ? gp.ntr * (gp.ntr + 1) : gp.ntr * gp.ntc;
+  gp.tiles_per_head = s.causal ? gp.ntr * (gp.ntr + 1) / 2 : gp.ntr * gp.ntc;
   gp.nwork = gp.tiles_per_head * s.hq;
   gp.grid = (gp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
   gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
