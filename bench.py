@@ -40,6 +40,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip timing xattn_full")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--only", choices=["score", "select", "sparse", "full", "copy"],
+                    help="profiling mode: run only this call `--steps` times (after one "
+                         "untimed pass of the path), print nothing but a short summary; "
+                         "`copy` copies a 1 GiB device buffer, the reference for scaling "
+                         "the HBM byte counters")
     return ap.parse_args()
 
 
@@ -111,6 +116,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     xattn.lib()
+    if args.only == "copy":
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "steps": args.steps}))
+        return
     t0 = time.perf_counter()
     w = generate(cfg)
     print(f"# generated config {cfg.cid} in {time.perf_counter() - t0:.1f}s", file=sys.stderr,
@@ -145,6 +161,26 @@ def main():
         if ev:
             ev[3].record(stream)
 
+    if args.only:
+        step()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            if args.only == "score":
+                xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores, workspace=ws,
+                                  stream=stream)
+            elif args.only == "select":
+                xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
+                                   stream=stream)
+            elif args.only == "sparse":
+                xattn.xattn_sparse_prefill(Q, K, V, cfg.B, idx, counts, cfg.causal, out=out,
+                                           stream=stream)
+            else:
+                xattn.xattn_full(Q, K, V, cfg.causal, out=out, stream=stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "config": cfg.cid, "steps": args.steps,
+                          "density": float(counts.to(torch.int64).sum()) /
+                          (hq * (NB * (NB + 1) // 2 if cfg.causal else NB * NB))}))
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
