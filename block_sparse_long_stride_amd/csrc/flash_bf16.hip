@@ -38,7 +38,7 @@ struct FlashParams {
   const int32_t* idx;      // nullptr: dense
   const int32_t* counts;
   int L, hq, group, NB, causal;
-  int nwork, grid;
+  int nwork, grid, interleave;
   float scale_log2;        // log2(e) / sqrt(d)
 };
 
@@ -107,15 +107,31 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
 
-  // Work order (kv group, query block descending, head within group): the
-  // XCD swizzle hands each XCD a contiguous range, so an XCD works on one KV
-  // group at a time and its L2 serves that group's K/V to all its CUs; within
-  // the group the longest causal rows start first.
-  const int w = xcd_swizzle(blockIdx.x, p.grid);
-  if (w >= p.nwork) return;
+  // Work order.  Items of one KV group are (query block descending, head),
+  // cut into chunks of 4 query blocks x all heads of the group.  Chunks are
+  // dealt round-robin to the 8 XCDs and every XCD runs through the groups in
+  // the same order, so (a) all XCDs work on the same KV group at a time -- its
+  // K/V stays resident in the memory-side cache -- and (b) the work-groups on
+  // one XCD share neighbouring query blocks and all heads of the group in its
+  // L2.  When the counts do not divide evenly, each XCD takes a contiguous
+  // range instead (one KV group per XCD).
   const int per_group = p.NB * p.group;
-  const int g = w / per_group;
-  const int rem = w % per_group;
+  int g, rem;
+  if (p.interleave) {
+    const int bid = blockIdx.x;
+    const int xcd = bid % kNumXcd, k = bid / kNumXcd;
+    const int per_xcd = per_group / kNumXcd;     // items of one group on one XCD
+    const int chunk = 4 * p.group;               // items per chunk
+    g = k / per_xcd;
+    const int kk = k % per_xcd;
+    rem = ((kk / chunk) * kNumXcd + xcd) * chunk + kk % chunk;
+    if (g >= p.hq / p.group) return;
+  } else {
+    const int w = xcd_swizzle(blockIdx.x, p.grid);
+    if (w >= p.nwork) return;
+    g = w / per_group;
+    rem = w % per_group;
+  }
   const int qb = p.NB - 1 - rem / p.group;
   const int h = g * p.group + rem % p.group;
 
@@ -346,6 +362,7 @@ hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const
   fp.causal = s.causal;
   fp.nwork = fp.NB * s.hq;
   fp.grid = (fp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
+  fp.interleave = (fp.NB * fp.group) % (kNumXcd * 4 * fp.group) == 0;
   fp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
   if (s.d == 128) return B == 128 ? launch<128, 128>(fp, st) : launch<128, 64>(fp, st);
   return B == 128 ? launch<64, 128>(fp, st) : launch<64, 64>(fp, st);
