@@ -5,8 +5,9 @@ bench's CPU-baseline leg, never by the library.
 """
 from .xattn_oracle import (Selection, antidiagonal_sums, approx_attention, block_mass,
                            block_scores, block_sparse_attention, find_blocks,
-                           full_attention, select_all, to_mask)
+                           find_blocks_topk, find_blocks_topratio, full_attention, select_all,
+                           to_mask, topratio_count)
 
 __all__ = ["Selection", "antidiagonal_sums", "approx_attention", "block_mass",
-           "block_scores", "block_sparse_attention", "find_blocks", "full_attention",
-           "select_all", "to_mask"]
+           "block_scores", "block_sparse_attention", "find_blocks", "find_blocks_topk",
+           "find_blocks_topratio", "full_attention", "select_all", "to_mask", "topratio_count"]

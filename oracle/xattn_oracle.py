@@ -26,6 +26,10 @@ Readings where the pages are silent (each is pinned by a test):
     tau never reached because of rounding) selects every valid block.
   * sparse attention: softmax at 1/sqrt(d) renormalised over the keys of the
     selected blocks (and j <= i when causal); a row with no key outputs 0.
+  * Top-K / Top-Ratio (the ablation's alternative cut rules, named but not
+    defined on the pages): the same ranking as find_blocks, cut at a fixed
+    count -- k blocks (K tokens / B), or the nearest integer to ratio * |valid|
+    -- clamped to [1, |valid|].
 """
 from __future__ import annotations
 
@@ -142,6 +146,42 @@ def find_blocks(mass_row: np.ndarray, n_valid: int, tau: float) -> Selection:
         k = int(hit[0]) + 1 if hit.size else n_valid
     sel = np.sort(order[:k])
     return Selection(selected=sel, kstar=k, order=order, csum=csum, n_valid=n_valid)
+
+
+def _ranked_prefix(mass_row: np.ndarray, n_valid: int, k: int) -> Selection:
+    """The first k valid blocks in the ranking of find_blocks (score
+    descending, lower block first on equal scores)."""
+    mass = np.asarray(mass_row, dtype=np.float64)[:n_valid]
+    kb = np.arange(n_valid)
+    order = np.lexsort((kb, -mass))
+    csum = np.cumsum(mass[order])
+    k = max(1, min(int(k), n_valid))
+    return Selection(selected=np.sort(order[:k]), kstar=k, order=order, csum=csum,
+                     n_valid=n_valid)
+
+
+def find_blocks_topk(mass_row: np.ndarray, n_valid: int, k_blocks: int) -> Selection:
+    """Top-K selection of the ablation on block selection strategies
+    (chapterpal.com Knowl 9, "Selection Strategy"; papercache.org summary,
+    ablation "block selection strategy"): a fixed number of key blocks per
+    query block, the k highest-scoring valid ones.  The pages give K in tokens
+    (8192); here k counts blocks (K / B).  A row with fewer valid blocks keeps
+    all of them; k >= 1."""
+    return _ranked_prefix(mass_row, n_valid, k_blocks)
+
+
+def topratio_count(n_valid: int, ratio: float) -> int:
+    """Blocks kept by Top-Ratio: the nearest integer to ratio * n_valid (halves
+    round up), at least 1 and at most n_valid.  Evaluated in float64 from the
+    float32 ratio, as floor(r * n + 0.5)."""
+    r = float(np.float32(ratio))
+    return max(1, min(n_valid, int(math.floor(r * n_valid + 0.5))))
+
+
+def find_blocks_topratio(mass_row: np.ndarray, n_valid: int, ratio: float) -> Selection:
+    """Top-Ratio selection of the same ablation (ratio 27% on the pages): the
+    highest-scoring topratio_count(n_valid, ratio) valid blocks of the row."""
+    return _ranked_prefix(mass_row, n_valid, topratio_count(n_valid, ratio))
 
 
 def select_all(scores: np.ndarray, causal: bool, tau: float,

@@ -247,6 +247,73 @@ def test_tau_one_selects_every_causal_block():
         assert int(words[0]) == (1 << (qb + 1)) - 1
 
 
+# --- Top-K / Top-Ratio cut rules (ablation "selection strategy") ------------
+@pytest.mark.parametrize("trial", range(40))
+def test_topk_is_a_best_k_subset_by_enumeration(trial):
+    """For every k, the Top-K set has the largest total mass of all k-subsets
+    (brute force), and it is the one the ranking picks: every selected block
+    outranks every unselected one by (mass desc, index asc)."""
+    rng = np.random.default_rng(3000 + trial)
+    n = int(rng.integers(1, 10))
+    mass = rng.dirichlet(np.full(n, float(rng.choice([0.3, 1.0, 5.0]))))
+    if trial % 4 == 0:                      # exact ties
+        mass = np.round(mass * 6) / 6
+    for k in range(1, n + 1):
+        sel = O.find_blocks_topk(mass, n, k)
+        assert sel.kstar == k and len(sel.selected) == k
+        best = max(sum(mass[list(c)]) for c in itertools.combinations(range(n), k))
+        assert math.isclose(float(mass[sel.selected].sum()), best, rel_tol=0, abs_tol=1e-12)
+        chosen = set(int(j) for j in sel.selected)
+        for a in chosen:
+            for b in set(range(n)) - chosen:
+                assert (mass[a] > mass[b]) or (mass[a] == mass[b] and a < b)
+
+
+def test_topk_clamps_to_valid_blocks():
+    mass = np.array([0.1, 0.4, 0.2, 0.3])
+    assert list(O.find_blocks_topk(mass, 4, 10).selected) == [0, 1, 2, 3]
+    assert list(O.find_blocks_topk(mass, 2, 5).selected) == [0, 1]     # causal row: 2 valid
+    assert list(O.find_blocks_topk(mass, 4, 1).selected) == [1]
+    assert list(O.find_blocks_topk(mass, 4, 2).selected) == [1, 3]
+
+
+def test_topk_agrees_with_threshold_cut():
+    """Cutting the ranking at the threshold rule's k* gives the threshold
+    rule's set (the two rules differ only in where the ranked prefix ends)."""
+    rng = np.random.default_rng(11)
+    L, d, S, B = 512, 16, 4, 32
+    Q, K = rng.standard_normal((L, d)) * 3, rng.standard_normal((L, d)) * 3
+    sc = O.block_scores(Q, K, S, B, causal=True)
+    for qb in range(sc.shape[0]):
+        for tau in (0.3, 0.8, 0.95):
+            thr = O.find_blocks(sc[qb], qb + 1, tau)
+            top = O.find_blocks_topk(sc[qb], qb + 1, thr.kstar)
+            assert list(top.selected) == list(thr.selected)
+
+
+@pytest.mark.parametrize("n,ratio,want", [
+    (100, 0.27, 27),      # float32(0.27) * 100 = 27.000001..., not 28
+    (1024, 0.27, 276),    # 276.48
+    (2, 0.27, 1), (1, 0.27, 1), (1, 1e-6, 1),     # at least one block
+    (10, 1.0, 10), (3, 0.5, 2), (7, 0.5, 4),      # halves round up
+    (8192, 0.27, 2212),   # 2211.84
+])
+def test_topratio_count_closed_form(n, ratio, want):
+    assert O.topratio_count(n, ratio) == want
+    assert O.find_blocks_topratio(np.linspace(1, 2, n), n, ratio).kstar == want
+
+
+def test_topk_tie_break_uniform_scores():
+    """Q = 0: every block scores 1/NB; Top-K keeps the k lowest key blocks."""
+    L, d, S, B = 256, 8, 4, 16
+    Q = np.zeros((L, d))
+    K = np.random.default_rng(2).standard_normal((L, d))
+    sc = O.block_scores(Q, K, S, B, causal=False)
+    for qb in range(sc.shape[0]):
+        assert list(O.find_blocks_topk(sc[qb], 16, 5).selected) == [0, 1, 2, 3, 4]
+        assert list(O.find_blocks_topratio(sc[qb], 16, 0.25).selected) == [0, 1, 2, 3]
+
+
 # --- block-sparse attention -------------------------------------------------
 def _naive_attention(Q, K, V, causal, allowed=None):
     L, d = Q.shape
