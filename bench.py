@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full", action="store_true", help="skip timing xattn_full")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the measurements of the NEXT rows (selection cut rules ...)")
     ap.add_argument("--only", choices=["score", "select", "sparse", "full", "copy"],
                     help="profiling mode: run only this call `--steps` times (after one "
                          "untimed pass of the path), print nothing but a short summary; "
@@ -222,6 +224,38 @@ def main():
         torch.cuda.synchronize()
         full_ms = ef[0].elapsed_time(ef[1])
 
+    # NEXT rows measured beside the headline (not part of the timed step)
+    next_rows = {}
+    if not args.no_next:
+        def timed(fn, reps=5):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            fn()
+            e[0].record(stream)
+            for _ in range(reps):
+                fn()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            return e[0].elapsed_time(e[1]) / reps
+
+        kblk = max(1, 8192 // cfg.B)
+        for name, fn in (
+                ("select_topk", lambda: xattn.xattn_select_topk(scores, kblk, cfg.causal, mask=mask,
+                                                                idx=idx, counts=counts, stream=stream)),
+                ("select_topratio", lambda: xattn.xattn_select_topratio(
+                    scores, 0.27, cfg.causal, mask=mask, idx=idx, counts=counts, stream=stream))):
+            ms_r = timed(fn)
+            n_r = int(counts.to(torch.int64).sum())
+            b_r = 4.0 * valid + mask.numel() * 8 + 4.0 * hq * NB * NB + 4.0 * hq * NB
+            next_rows["f1_" + name] = {
+                "param": f"K={kblk * cfg.B} tokens ({kblk} blocks)" if name == "select_topk"
+                         else "ratio=0.27",
+                "ms": round(ms_r, 3), "gbs": round(b_r / (ms_r * 1e-3) / 1e9, 1),
+                "density": round(n_r / valid, 5)}
+        # restore the threshold selection for anything that follows
+        xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
+                           stream=stream)
+        torch.cuda.synchronize()
+
     tflops = F_full / (wall_ms * 1e-3) / 1e12
     achieved = F_sparse / (sparse_ms * 1e-3) / 1e12
     res = {
@@ -266,6 +300,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("flash_bf16", f"config{cfg.cid}")},
         "cpu_baseline": None,
+        "next_rows": next_rows or None,
     }
     if not args.no_cpu_baseline:
         ms_cpu, rows, threads = cpu_baseline(cfg, w, args.cpu_sample_seconds)

@@ -32,6 +32,12 @@ struct TauArray {
 };
 hipError_t launch_select(int hq, int NB, int causal, const float* scores, const TauArray& tau,
                          uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
+// Fixed-count cut rules on the same ranking: Top-K (k blocks) and Top-Ratio
+// (the nearest integer to ratio * valid blocks), both clamped to [1, valid].
+hipError_t launch_select_topk(int hq, int NB, int causal, const float* scores, int k_blocks,
+                              uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
+hipError_t launch_select_topratio(int hq, int NB, int causal, const float* scores, float ratio,
+                                  uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
 
 // ---- attention ---------------------------------------------------------------
 // idx == nullptr selects dense mode (every key block, causal-limited).

@@ -8,6 +8,13 @@
 // block id, so equal scores keep the lower block first), forms the prefix sums
 // of the ranked scores in float64, cuts at the first prefix >= tau, and emits
 // the bitmask, the ascending block ids (padded with -1) and the count.
+//
+// The same kernel serves the two fixed-count cut rules of the ablation on
+// block selection strategies (chapterpal.com Knowl 9, "Selection Strategy";
+// papercache.org summary, ablation "block selection strategy"): Top-K keeps
+// the k highest-ranked blocks, Top-Ratio the nearest integer to ratio times
+// the number of valid blocks (halves up); both keep at least one and at most
+// every valid block.
 #include "common.h"
 #include "launch.h"
 
@@ -16,13 +23,18 @@ namespace {
 
 constexpr int kThreads = 256;
 
+enum CutRule : int { kThreshold = 0, kTopK = 1, kTopRatio = 2 };
+
 struct SelectParams {
   const float* scores;
   uint64_t* mask;
   int32_t* idx;
   int32_t* counts;
   int NB, causal, nwords;
-  TauArray tau;
+  int rule;        // CutRule
+  int topk;        // kTopK: blocks kept
+  float ratio;     // kTopRatio: share of the valid blocks kept
+  TauArray tau;    // kThreshold: per-head tau
 };
 
 // monotone map of float bits to unsigned (total order for finite values)
@@ -75,8 +87,13 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p) {
     }
   }
 
+  if (p.rule != kThreshold) {   // fixed count: no prefix sums needed
+    int k = p.rule == kTopK ? p.topk : (int)floor((double)p.ratio * (double)n + 0.5);
+    k = k < 1 ? 1 : (k > n ? n : k);
+    if (tid == 0) s_cut = k;
+  }
   // prefix sums in float64 over the ranked scores: a contiguous chunk per thread
-  const float tau = p.tau.v[h];
+  const float tau = p.rule == kThreshold ? p.tau.v[h] : 1.0f;
   const int per = (n + kThreads - 1) / kThreads;
   const int b0 = tid * per, b1 = min(n, b0 + per);
   double local = 0.0;
@@ -143,11 +160,9 @@ hipError_t launch_cap(const SelectParams& sp, int rows, hipStream_t st) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_select(int hq, int NB, int causal, const float* scores, const TauArray& tau,
-                         uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st) {
-  SelectParams sp;
+SelectParams make_params(int NB, int causal, const float* scores, uint64_t* mask, int32_t* idx,
+                         int32_t* counts) {
+  SelectParams sp{};
   sp.scores = scores;
   sp.mask = mask;
   sp.idx = idx;
@@ -155,11 +170,39 @@ hipError_t launch_select(int hq, int NB, int causal, const float* scores, const 
   sp.NB = NB;
   sp.causal = causal;
   sp.nwords = (NB + 63) / 64;
-  sp.tau = tau;
-  const int rows = hq * NB;
-  if (NB <= 256) return launch_cap<256>(sp, rows, st);
-  if (NB <= 1024) return launch_cap<1024>(sp, rows, st);
+  return sp;
+}
+
+hipError_t launch_rows(const SelectParams& sp, int rows, hipStream_t st) {
+  if (sp.NB <= 256) return launch_cap<256>(sp, rows, st);
+  if (sp.NB <= 1024) return launch_cap<1024>(sp, rows, st);
   return launch_cap<4096>(sp, rows, st);
+}
+
+}  // namespace
+
+hipError_t launch_select(int hq, int NB, int causal, const float* scores, const TauArray& tau,
+                         uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st) {
+  SelectParams sp = make_params(NB, causal, scores, mask, idx, counts);
+  sp.rule = kThreshold;
+  sp.tau = tau;
+  return launch_rows(sp, hq * NB, st);
+}
+
+hipError_t launch_select_topk(int hq, int NB, int causal, const float* scores, int k_blocks,
+                              uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st) {
+  SelectParams sp = make_params(NB, causal, scores, mask, idx, counts);
+  sp.rule = kTopK;
+  sp.topk = k_blocks;
+  return launch_rows(sp, hq * NB, st);
+}
+
+hipError_t launch_select_topratio(int hq, int NB, int causal, const float* scores, float ratio,
+                                  uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st) {
+  SelectParams sp = make_params(NB, causal, scores, mask, idx, counts);
+  sp.rule = kTopRatio;
+  sp.ratio = ratio;
+  return launch_rows(sp, hq * NB, st);
 }
 
 }  // namespace xattn

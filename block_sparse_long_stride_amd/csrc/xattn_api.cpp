@@ -147,6 +147,40 @@ xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* s
   return hip_status(e, "xattn_select launch");
 }
 
+static xattn_status check_select_args(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                                      const void* mask, const void* idx, const void* counts) {
+  if (hq < 1 || NB < 1) return fail(XATTN_EINVAL, "hq (%d) and NB (%d) must be >= 1", hq, NB);
+  if (causal != 0 && causal != 1) return fail(XATTN_EINVAL, "causal must be 0 or 1");
+  if (!scores || !mask || !idx || !counts)
+    return fail(XATTN_EINVAL, "scores, mask, idx and counts must be non-NULL");
+  if (NB > xattn::kMaxSelectBlocks)
+    return fail(XATTN_EUNSUPPORTED, "selection covers NB <= %d, got %d", xattn::kMaxSelectBlocks, NB);
+  return XATTN_OK;
+}
+
+xattn_status xattn_select_topk(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                               int32_t k_blocks, uint64_t* mask, int32_t* idx, int32_t* counts,
+                               void* stream) {
+  xattn_status st = check_select_args(hq, NB, causal, scores, mask, idx, counts);
+  if (st != XATTN_OK) return st;
+  if (k_blocks < 1) return fail(XATTN_EINVAL, "k_blocks = %d must be >= 1", k_blocks);
+  hipError_t e = xattn::launch_select_topk(hq, NB, causal, scores, k_blocks, mask, idx, counts,
+                                           (hipStream_t)stream);
+  return hip_status(e, "xattn_select_topk launch");
+}
+
+xattn_status xattn_select_topratio(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                                   float ratio, uint64_t* mask, int32_t* idx, int32_t* counts,
+                                   void* stream) {
+  xattn_status st = check_select_args(hq, NB, causal, scores, mask, idx, counts);
+  if (st != XATTN_OK) return st;
+  if (!(ratio > 0.0f && ratio <= 1.0f))
+    return fail(XATTN_EINVAL, "ratio = %g is outside (0, 1]", (double)ratio);
+  hipError_t e = xattn::launch_select_topratio(hq, NB, causal, scores, ratio, mask, idx, counts,
+                                               (hipStream_t)stream);
+  return hip_status(e, "xattn_select_topratio launch");
+}
+
 xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
                                   const void* V, int32_t B, const int32_t* idx,
                                   const int32_t* counts, void* O, void* stream) {

@@ -17,9 +17,9 @@ XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EWORKSPACE, XATTN_EHIP = range
 XATTN_FP32, XATTN_BF16 = 0, 1
 
 # every entry point declared in include/xattn.h
-EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_select",
-           "xattn_sparse_prefill", "xattn_full", "xattn_status_str", "xattn_last_error",
-           "xattn_version")
+EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_select", "xattn_select_topk",
+           "xattn_select_topratio", "xattn_sparse_prefill", "xattn_full", "xattn_status_str",
+           "xattn_last_error", "xattn_version")
 
 
 class XattnError(RuntimeError):
@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.xattn_score.restype = I32
     L.xattn_select.argtypes = [I32, I32, I32, P, P, P, P, P, P]
     L.xattn_select.restype = I32
+    L.xattn_select_topk.argtypes = [I32, I32, I32, P, I32, P, P, P, P]
+    L.xattn_select_topk.restype = I32
+    L.xattn_select_topratio.argtypes = [I32, I32, I32, P, ctypes.c_float, P, P, P, P]
+    L.xattn_select_topratio.restype = I32
     L.xattn_sparse_prefill.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.xattn_sparse_prefill.restype = I32
     L.xattn_full.argtypes = [SP, P, P, P, P, P]
@@ -144,6 +148,41 @@ def xattn_select(scores, tau: Sequence[float], causal: bool, mask=None, idx=None
     _check(lib().xattn_select(hq, NB, int(bool(causal)), _ptr(scores),
                               tau_np.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(idx),
                               _ptr(counts), _stream(stream)), "xattn_select")
+    return mask, idx, counts
+
+
+def _select_outputs(scores, mask, idx, counts):
+    torch = _torch()
+    hq, NB = scores.shape[0], scores.shape[1]
+    if not (scores.is_cuda and scores.is_contiguous() and scores.dtype == torch.float32):
+        raise ValueError("scores must be a contiguous fp32 device tensor")
+    words = (NB + 63) // 64
+    if mask is None:
+        mask = torch.empty((hq, NB, words), dtype=torch.int64, device=scores.device)
+    if idx is None:
+        idx = torch.empty((hq, NB, NB), dtype=torch.int32, device=scores.device)
+    if counts is None:
+        counts = torch.empty((hq, NB), dtype=torch.int32, device=scores.device)
+    return hq, NB, mask, idx, counts
+
+
+def xattn_select_topk(scores, k_blocks: int, causal: bool, mask=None, idx=None, counts=None,
+                      stream=None) -> Tuple:
+    """Top-K cut (k_blocks blocks per query block) of the selection ranking."""
+    hq, NB, mask, idx, counts = _select_outputs(scores, mask, idx, counts)
+    _check(lib().xattn_select_topk(hq, NB, int(bool(causal)), _ptr(scores), int(k_blocks),
+                                   _ptr(mask), _ptr(idx), _ptr(counts), _stream(stream)),
+           "xattn_select_topk")
+    return mask, idx, counts
+
+
+def xattn_select_topratio(scores, ratio: float, causal: bool, mask=None, idx=None, counts=None,
+                          stream=None) -> Tuple:
+    """Top-Ratio cut (nearest integer to ratio x valid blocks) of the selection ranking."""
+    hq, NB, mask, idx, counts = _select_outputs(scores, mask, idx, counts)
+    _check(lib().xattn_select_topratio(hq, NB, int(bool(causal)), _ptr(scores), float(ratio),
+                                       _ptr(mask), _ptr(idx), _ptr(counts), _stream(stream)),
+           "xattn_select_topratio")
     return mask, idx, counts
 
 

@@ -11,6 +11,8 @@
  * Calls, in the order of the path:
  *   xattn_score          block scores from strided antidiagonal sums
  *   xattn_select         threshold block selection -> mask, index lists
+ *   xattn_select_topk    Top-K cut of the same ranking (selection ablation)
+ *   xattn_select_topratio  Top-Ratio cut of the same ranking
  *   xattn_sparse_prefill attention over the selected blocks
  *   xattn_full           dense attention (the speed baseline)
  *
@@ -102,6 +104,27 @@ xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
 xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* scores,
                           const float* tau_host, uint64_t* mask, int32_t* idx,
                           int32_t* counts, void* stream);
+
+/*
+ * Fixed-count cut rules compared with the threshold rule in the ablation on
+ * block selection strategies (chapterpal.com Knowl 9, "Selection Strategy":
+ * Top-K with K = 8192 tokens, Top-Ratio with ratio 27%; papercache.org
+ * summary, ablation "block selection strategy").  The pages name the rules
+ * without defining them; here both cut the ranking of xattn_select (score
+ * descending, lower kb first on ties) at a fixed count, clamped to
+ * [1, valid blocks]:
+ *   xattn_select_topk      k_blocks blocks (K tokens / B), k_blocks >= 1
+ *   xattn_select_topratio  floor(ratio * valid + 0.5) blocks, evaluated in
+ *                          float64, ratio in (0, 1]
+ * Arguments, outputs, limits and errors otherwise as xattn_select
+ * (no per-head tau; hq is not limited to 128).
+ */
+xattn_status xattn_select_topk(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                               int32_t k_blocks, uint64_t* mask, int32_t* idx, int32_t* counts,
+                               void* stream);
+xattn_status xattn_select_topratio(int32_t hq, int32_t NB, int32_t causal, const float* scores,
+                                   float ratio, uint64_t* mask, int32_t* idx, int32_t* counts,
+                                   void* stream);
 
 /*
  * Block-sparse attention (section 1, step 3): for query block qb of head h,

@@ -94,6 +94,32 @@ def test_select_rejects():
     assert call(hq=129, tau=np.full(129, 0.9)) == X.XATTN_EUNSUPPORTED
 
 
+def test_select_cut_rules_reject():
+    lib = X.lib()
+
+    def topk(hq=2, NB=8, causal=1, k=4, null=False):
+        return lib.xattn_select_topk(hq, NB, causal, DUMMY, k, None if null else DUMMY, DUMMY,
+                                     DUMMY, None)
+
+    def ratio(hq=2, NB=8, causal=1, r=0.27, null=False):
+        return lib.xattn_select_topratio(hq, NB, causal, DUMMY, r, DUMMY, DUMMY,
+                                         None if null else DUMMY, None)
+
+    assert topk(k=0) == X.XATTN_EINVAL
+    assert topk(k=-3) == X.XATTN_EINVAL
+    assert topk(NB=0) == X.XATTN_EINVAL
+    assert topk(causal=2) == X.XATTN_EINVAL
+    assert topk(null=True) == X.XATTN_EINVAL
+    assert topk(NB=4097) == X.XATTN_EUNSUPPORTED
+    assert ratio(r=0.0) == X.XATTN_EINVAL
+    assert ratio(r=1.01) == X.XATTN_EINVAL
+    assert ratio(r=float("nan")) == X.XATTN_EINVAL
+    assert ratio(hq=0) == X.XATTN_EINVAL
+    assert ratio(null=True) == X.XATTN_EINVAL
+    assert ratio(NB=5000) == X.XATTN_EUNSUPPORTED
+    assert b"k_blocks" in lib.xattn_last_error() or b"NB" in lib.xattn_last_error()
+
+
 def test_attention_rejects():
     lib = X.lib()
     sh = _shape()

@@ -144,6 +144,35 @@ def test_fullsize_select_on_oracle_scores(fullsize):
                                       O.to_mask(sel, cfg.nb))
 
 
+def test_fullsize_cut_rules_on_oracle_scores(fullsize):
+    """Top-K (8192 tokens) and Top-Ratio (27%), the ablation's settings, on
+    the oracle's fp32 score rows: sampled rows match exactly."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_select_topk, xattn_select_topratio
+    cfg, w, dev, r = fullsize
+    s = torch.zeros((cfg.hq, cfg.nb, cfg.nb), dtype=torch.float32, device="cuda")
+    rows32 = {}
+    for key in r["pairs"]:
+        rows32[key] = r["ora"][key].astype(np.float32)
+        s[key[0], key[1]] = torch.from_numpy(rows32[key]).cuda()
+    kblk = max(1, 8192 // cfg.B)
+    for rule in ("topk", "ratio"):
+        if rule == "topk":
+            mask, idx, counts = xattn_select_topk(s, kblk, cfg.causal)
+        else:
+            mask, idx, counts = xattn_select_topratio(s, 0.27, cfg.causal)
+        _sync()
+        for h, qb in r["pairs"]:
+            nv = qb + 1 if cfg.causal else cfg.nb
+            row = rows32[(h, qb)].astype(np.float64)
+            sel = (O.find_blocks_topk(row, nv, kblk) if rule == "topk"
+                   else O.find_blocks_topratio(row, nv, 0.27))
+            assert int(counts[h, qb]) == sel.kstar
+            assert list(idx[h, qb, :sel.kstar].cpu().numpy()) == list(sel.selected)
+            np.testing.assert_array_equal(mask[h, qb].cpu().numpy().view(np.uint64),
+                                          O.to_mask(sel, cfg.nb))
+
+
 def test_fullsize_sparse_prefill(fullsize):
     """Sparse prefill on the oracle's selections of the sampled rows (other
     rows get empty lists) against oracle attention over the same blocks."""

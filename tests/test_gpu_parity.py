@@ -86,6 +86,38 @@ def test_select_matches_oracle_on_same_scores(name):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
+def test_cut_rules_match_oracle_on_same_scores(name):
+    """Top-K and Top-Ratio on the same fp32 scores: masks, idx and counts are
+    exact, for counts below, inside and beyond the valid range."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_select_topk, xattn_select_topratio
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] cut rules", flush=True)
+    s32 = ora.astype(np.float32)
+    sd = torch.from_numpy(s32).cuda()
+    NB = cfg.nb
+    runs = [("topk", k) for k in (1, max(1, NB // 4), NB + 5)] + \
+           [("ratio", r) for r in (0.27, 1.0, 1e-3)]
+    for rule, par in runs:
+        if rule == "topk":
+            mask, idx, counts = xattn_select_topk(sd, par, cfg.causal)
+        else:
+            mask, idx, counts = xattn_select_topratio(sd, par, cfg.causal)
+        _sync()
+        mask, idx, counts = mask.cpu().numpy(), idx.cpu().numpy(), counts.cpu().numpy()
+        for h in range(cfg.hq):
+            for qb in range(NB):
+                nv = qb + 1 if cfg.causal else NB
+                row = s32[h, qb].astype(np.float64)
+                sel = (O.find_blocks_topk(row, nv, par) if rule == "topk"
+                       else O.find_blocks_topratio(row, nv, par))
+                assert counts[h, qb] == sel.kstar, (rule, par, h, qb)
+                assert list(idx[h, qb, :sel.kstar]) == list(sel.selected), (rule, par, h, qb)
+                assert np.all(idx[h, qb, sel.kstar:] == -1), (rule, par, h, qb)
+                np.testing.assert_array_equal(mask[h, qb].view(np.uint64), O.to_mask(sel, NB))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
 def test_pipeline_masks_match_oracle(name):
     """GPU score -> GPU select against the oracle's fp64 path, with band counts."""
     from block_sparse_long_stride_amd import xattn_select
