@@ -5,9 +5,10 @@ bench's CPU-baseline leg, never by the library.
 """
 from .xattn_oracle import (Selection, antidiagonal_sums, approx_attention, block_mass,
                            block_scores, block_sparse_attention, find_blocks,
-                           find_blocks_topk, find_blocks_topratio, full_attention, select_all,
-                           to_mask, topratio_count)
+                           find_blocks_topk, find_blocks_topratio, full_attention, pattern_sums,
+                           select_all, to_mask, topratio_count)
 
 __all__ = ["Selection", "antidiagonal_sums", "approx_attention", "block_mass",
            "block_scores", "block_sparse_attention", "find_blocks", "find_blocks_topk",
-           "find_blocks_topratio", "full_attention", "select_all", "to_mask", "topratio_count"]
+           "find_blocks_topratio", "full_attention", "pattern_sums", "select_all", "to_mask",
+           "topratio_count"]

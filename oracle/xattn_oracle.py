@@ -26,6 +26,9 @@ Readings where the pages are silent (each is pinned by a test):
     tau never reached because of rounding) selects every valid block.
   * sparse attention: softmax at 1/sqrt(d) renormalised over the keys of the
     selected blocks (and j <= i when causal); a row with no key outputs 0.
+  * sampling patterns other than the antidiagonal (named, not defined, in the
+    pattern ablation): diagonal = key sub-row a for query sub-row a; random =
+    a seeded permutation of the key sub-rows, drawn by the caller.
   * Top-K / Top-Ratio (the ablation's alternative cut rules, named but not
     defined on the pages): the same ranking as find_blocks, cut at a fixed
     count -- k blocks (K tokens / B), or the nearest integer to ratio * |valid|
@@ -63,6 +66,27 @@ def antidiagonal_sums(Q: np.ndarray, K: np.ndarray, S: int,
     return A
 
 
+def pattern_sums(Q: np.ndarray, K: np.ndarray, S: int, phase: Sequence[int],
+                 rows: Optional[range] = None) -> np.ndarray:
+    """A[R, c] = sum_{a<S} <Q[R*S + a], K[c*S + phase[a]]>: the SxS tile of
+    Q K^T sampled at one entry per query sub-row a, the key sub-row given by
+    the permutation `phase`.  Sampling patterns of the ablation on pattern
+    geometry (chapterpal.com Knowl 9, "Pattern Geometry": antidiagonal,
+    diagonal and random sampling at the same stride; papercache.org summary,
+    ablation on the antidiagonal pattern): phase[a] = S-1-a is the antidiagonal
+    of antidiagonal_sums, phase[a] = a the main diagonal, a seeded random
+    permutation the random pattern (one sample per query and key sub-row)."""
+    phase = [int(x) for x in phase]
+    assert sorted(phase) == list(range(S)), "phase must be a permutation of 0..S-1"
+    rows = range(Q.shape[0] // S) if rows is None else rows
+    r0, r1 = rows.start, rows.stop
+    Lk = K.shape[0] // S
+    A = np.zeros((r1 - r0, Lk), dtype=np.float64)
+    for a in range(S):
+        A += Q[r0 * S + a: r1 * S: S] @ K[phase[a]: Lk * S: S].T
+    return A
+
+
 # ---------------------------------------------------------------------------
 # Step 2 -- A_approx = Softmax(A / sqrt(d_h * S)) per reshaped row (Algorithm 1),
 # with the causal reading c > R masked.
@@ -91,13 +115,15 @@ def block_mass(P: np.ndarray, B: int, S: int) -> np.ndarray:
 
 
 def block_scores(Q: np.ndarray, K: np.ndarray, S: int, B: int, causal: bool,
-                 qblocks: Optional[Sequence[int]] = None, chunk: int = 64) -> np.ndarray:
+                 qblocks: Optional[Sequence[int]] = None, chunk: int = 64,
+                 phase: Optional[Sequence[int]] = None) -> np.ndarray:
     """Block scores [len(qblocks)][NB] of one head (Q: its queries, K: its group's keys).
 
     Follows Algorithm 1 per query block b: reshaped product, scaled softmax,
     then the tile sums that find_blocks takes.  Causal entries kb > qb are 0.
     Consecutive query blocks are evaluated `chunk` at a time (their rows do
-    not interact).
+    not interact).  `phase` (default: the antidiagonal) selects another
+    sampling pattern through pattern_sums; the rest is unchanged.
     """
     L, d = Q.shape
     NB = L // B
@@ -110,7 +136,8 @@ def block_scores(Q: np.ndarray, K: np.ndarray, S: int, B: int, causal: bool,
         while j < len(qblocks) and j - i < chunk and qblocks[j] == qblocks[j - 1] + 1:
             j += 1
         b0, b1 = qblocks[i], qblocks[j - 1] + 1
-        A = antidiagonal_sums(Q, K, S, range(b0 * bs, b1 * bs))
+        rr = range(b0 * bs, b1 * bs)
+        A = antidiagonal_sums(Q, K, S, rr) if phase is None else pattern_sums(Q, K, S, phase, rr)
         P = approx_attention(A, d, S, causal, b0 * bs)
         out[i:j] = block_mass(P, B, S)
         i = j

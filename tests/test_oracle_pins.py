@@ -65,6 +65,71 @@ def test_antidiagonal_sums_brute_force_tile_antidiagonals(S):
             assert A[R, c] == tot
 
 
+def _perm(S, kind, seed=0):
+    if kind == "antidiagonal":
+        return [S - 1 - a for a in range(S)]
+    if kind == "diagonal":
+        return list(range(S))
+    return [int(x) for x in np.random.default_rng(seed).permutation(S)]
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("kind", ["antidiagonal", "diagonal", "random"])
+def test_pattern_sums_brute_force_tile_samples(S, kind):
+    """Q = M, K = I: A[R, c] is the sum of M over the tile entries (RS + a,
+    cS + phase[a]), by explicit loops; the antidiagonal phase reproduces
+    antidiagonal_sums exactly."""
+    rng = np.random.default_rng(31 + S)
+    L = 4 * S * 2
+    M = rng.integers(-50, 51, size=(L, L)).astype(np.float64)
+    ph = _perm(S, kind, seed=S)
+    A = O.pattern_sums(M, np.eye(L), S, ph)
+    for R in range(L // S):
+        for c in range(L // S):
+            tot = 0.0
+            for a in range(S):
+                tot += M[R * S + a, c * S + ph[a]]
+            assert A[R, c] == tot
+    if kind == "antidiagonal":
+        np.testing.assert_array_equal(A, O.antidiagonal_sums(M, np.eye(L), S))
+
+
+@pytest.mark.parametrize("S", [2, 4, 8])
+def test_diagonal_pattern_samples_every_sth_diagonal(S):
+    """The diagonal pattern sums exactly the entries with (i - j) mod S == 0,
+    which include the main diagonal (i == j) that the antidiagonal pattern
+    never samples for even S."""
+    rng = np.random.default_rng(5 + S)
+    L = 6 * S
+    M = rng.integers(-20, 21, size=(L, L)).astype(np.float64)
+    A = O.pattern_sums(M, np.eye(L), S, list(range(S)))
+    for R in range(L // S):
+        for c in range(L // S):
+            tot = sum(M[i, j] for i in range(R * S, (R + 1) * S)
+                      for j in range(c * S, (c + 1) * S) if (i - j) % S == 0)
+            assert A[R, c] == tot
+
+
+@pytest.mark.parametrize("kind", ["antidiagonal", "diagonal", "random"])
+def test_pattern_block_scores_rows_sum_to_one(kind):
+    rng = np.random.default_rng(9)
+    L, d, S, B = 512, 16, 8, 64
+    Q, K = rng.standard_normal((L, d)) * 2, rng.standard_normal((L, d)) * 2
+    ph = _perm(S, kind, seed=3)
+    for causal in (True, False):
+        sc = O.block_scores(Q, K, S, B, causal, phase=ph)
+        np.testing.assert_allclose(sc.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        if causal:
+            assert np.all(np.triu(sc, 1) == 0)
+        if kind == "antidiagonal":
+            np.testing.assert_array_equal(sc, O.block_scores(Q, K, S, B, causal))
+
+
+def test_pattern_rejects_non_permutation():
+    with pytest.raises(AssertionError):
+        O.pattern_sums(np.zeros((8, 2)), np.zeros((8, 2)), 4, [0, 1, 1, 2])
+
+
 @pytest.mark.parametrize("S,B", [(2, 8), (4, 8), (4, 16), (8, 16), (8, 64)])
 def test_sampled_set_invariants(S, B):
     """Which entries of Q K^T the scores sum: every key is hit exactly once per
