@@ -251,6 +251,23 @@ def main():
                          else "ratio=0.27",
                 "ms": round(ms_r, 3), "gbs": round(b_r / (ms_r * 1e-3) / 1e9, 1),
                 "density": round(n_r / valid, 5)}
+        # sampling patterns of the pattern ablation: same scoring kernel, another
+        # key sub-row per query sub-row; density of the threshold selection
+        rng_p = np.random.default_rng(2024)
+        for name, ph in (("diagonal", list(range(cfg.S))),
+                         ("random", [int(x) for x in rng_p.permutation(cfg.S)])):
+            ms_p = timed(lambda: xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores,
+                                                   workspace=ws, stream=stream, phase=ph))
+            xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
+                               stream=stream)
+            torch.cuda.synchronize()
+            n_p = int(counts.to(torch.int64).sum())
+            next_rows["f3_score_" + name] = {
+                "phase": ph, "ms": round(ms_p, 3),
+                "tflops": round(F_score / (ms_p * 1e-3) / 1e12, 1),
+                "frac_bf16_peak": round(F_score / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "density_threshold_select": round(n_p / valid, 5)}
+        xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores, workspace=ws, stream=stream)
         # restore the threshold selection for anything that follows
         xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
                            stream=stream)

@@ -18,11 +18,19 @@ struct Shape {
 //   P: [NB][32] fp32 partial block sums (each against its own snapshot max)
 //   M: [nct][32] fp32 snapshot max (log2 units) per 64-column range
 //   Z: [nct][32] fp32 snapshot sum of exp2 against that max
+// Sampling pattern of the scoring product: key sub-row paired with query
+// sub-row a inside each SxS tile.  custom == 0 is the antidiagonal, S-1-a;
+// otherwise v[0 .. S) is a permutation of 0 .. S-1 (S <= kMaxPhase).
+constexpr int kMaxPhase = 64;
+struct PhaseMap {
+  int32_t custom;
+  int32_t v[kMaxPhase];
+};
 size_t score_workspace_bytes(const Shape& s, int S, int B);
 hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
-                             float* scores, void* ws, hipStream_t st);
+                             const PhaseMap& phase, float* scores, void* ws, hipStream_t st);
 hipError_t launch_score_fp32(const Shape& s, const void* Q, const void* K, int S, int B,
-                             float* scores, hipStream_t st);
+                             const PhaseMap& phase, float* scores, hipStream_t st);
 
 // ---- selection --------------------------------------------------------------
 constexpr int kMaxHeads = 128;

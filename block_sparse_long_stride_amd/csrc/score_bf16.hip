@@ -9,7 +9,9 @@
 // K-dimension S*d: the query operand is Q's own memory read as an (L/S) x (S*d)
 // matrix, and the key operand reads sub-row S-1-a of key group c for feature
 // chunk a -- the reshape is folded into the global load addresses and never
-// materialised.
+// materialised.  Other sampling patterns of the pattern-geometry ablation
+// (chapterpal.com Knowl 9: diagonal, random) only change which key sub-row a
+// chunk reads (a permutation of 0 .. S-1), so they run the same kernel.
 //
 // Kernel 1 (score_gemm): MFMA 32x32x16 bf16 GEMM over lower-triangular (causal)
 // or all 128x128 tiles of the reshaped matrix, computed transposed (rows =
@@ -48,6 +50,7 @@ struct GemmParams {
   int L, S, group, NB, Lr, nR32, nct;
   int causal, ntr, ntc, tiles_per_head, nwork, grid;
   float scale_log2;
+  PhaseMap phase;   // key sub-row per query sub-row (default: antidiagonal)
 };
 
 // LDS rows hold one 32-element (64-byte) chunk of a reshaped row; their four
@@ -129,8 +132,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
     kc = min(kc, nk - 1);   // past the end: harmless reload, keeps the copy count fixed
     const int f0 = kc * kKC;
     const int a = f0 / D, e0 = f0 % D;
-    // key operand: sub-row S-1-a of key group c (the stride reshape, reversed phase)
-    const uint32_t koff = (uint32_t)(((p.S - 1 - a) * D + e0) * 2);
+    // key operand: sub-row S-1-a of key group c (the stride reshape, reversed
+    // phase), or the sub-row the sampling pattern pairs with query sub-row a
+    const int ka = p.phase.custom ? p.phase.v[a] : p.S - 1 - a;
+    const uint32_t koff = (uint32_t)((ka * D + e0) * 2);
     const uint32_t qoff = (uint32_t)(f0 * 2);
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
@@ -400,7 +405,7 @@ size_t score_workspace_bytes(const Shape& s, int S, int B) {
 }
 
 hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
-                             float* scores, void* ws, hipStream_t st) {
+                             const PhaseMap& phase, float* scores, void* ws, hipStream_t st) {
   const WsLayout wl = ws_layout(s, S, B);
   float* P = (float*)ws;
   float* M = P + wl.p_elems;
@@ -426,6 +431,7 @@ hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S
   gp.nwork = gp.tiles_per_head * s.hq;
   gp.grid = (gp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
   gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
+  gp.phase = phase;
   const int bs = B / S;
   hipError_t e = (s.d == 128) ? launch_gemm_bs<128>(gp, bs, st) : launch_gemm_bs<64>(gp, bs, st);
   if (e != hipSuccess) return e;

@@ -21,13 +21,15 @@ struct Fp32ScoreParams {
   float* scores;
   int L, d, S, bs, NB, Lr, group, causal;
   float scale_log2;
+  PhaseMap phase;   // key sub-row per query sub-row (default: antidiagonal)
 };
 
-__device__ float reshaped_dot(const float* Qh, const float* Kg, int R, int c, int S, int d) {
+__device__ float reshaped_dot(const float* Qh, const float* Kg, int R, int c, int S, int d,
+                             const PhaseMap& ph) {
   float acc = 0.f;
   for (int a = 0; a < S; ++a) {
     const float* q = Qh + (size_t)(R * S + a) * d;
-    const float* k = Kg + (size_t)(c * S + (S - 1 - a)) * d;
+    const float* k = Kg + (size_t)(c * S + (ph.custom ? ph.v[a] : S - 1 - a)) * d;
     for (int e = 0; e < d; ++e) acc = fmaf(q[e], k[e], acc);
   }
   return acc;
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void score_fp32_kernel(Fp32ScoreParams p)
     const int lim = p.causal ? R + 1 : p.Lr;
     float m = -INFINITY, z = 0.f;
     for (int c = tid; c < lim; c += kThreads) {
-      const float x = reshaped_dot(Qh, Kg, R, c, p.S, p.d) * p.scale_log2;
+      const float x = reshaped_dot(Qh, Kg, R, c, p.S, p.d, p.phase) * p.scale_log2;
       if (x > m) {
         z = z * fast_exp2(m - x) + 1.f;
         m = x;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(kThreads) void score_fp32_kernel(Fp32ScoreParams p)
         const int R = qb * p.bs + r;
         for (int c = kb * p.bs; c < (kb + 1) * p.bs && c < ncols; ++c) {
           if (p.causal && c > R) continue;
-          const float x = reshaped_dot(Qh, Kg, R, c, p.S, p.d) * p.scale_log2;
+          const float x = reshaped_dot(Qh, Kg, R, c, p.S, p.d, p.phase) * p.scale_log2;
           acc += fast_exp2(x - row_m[r]) * row_invz[r];
         }
       }
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void score_fp32_kernel(Fp32ScoreParams p)
 }  // namespace
 
 hipError_t launch_score_fp32(const Shape& s, const void* Q, const void* K, int S, int B,
-                             float* scores, hipStream_t st) {
+                             const PhaseMap& phase, float* scores, hipStream_t st) {
   Fp32ScoreParams p;
   p.Q = (const float*)Q;
   p.K = (const float*)K;
@@ -118,6 +120,7 @@ hipError_t launch_score_fp32(const Shape& s, const void* Q, const void* K, int S
   p.group = s.hq / s.hkv;
   p.causal = s.causal;
   p.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
+  p.phase = phase;
   hipLaunchKernelGGL(score_fp32_kernel, dim3(s.hq * p.NB), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }

@@ -106,9 +106,10 @@ size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t 
   return xattn::score_workspace_bytes(s, S, B);
 }
 
-xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
-                         int32_t B, float* scores, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+static xattn_status run_score(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
+                              int32_t B, const xattn::PhaseMap& phase, float* scores,
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              const char* what) {
   xattn::Shape s;
   xattn_status st = check_score_args(shape, S, B, &s);
   if (st != XATTN_OK) return st;
@@ -118,9 +119,38 @@ xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
   if (workspace_bytes < need)
     return fail(XATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   hipStream_t hs = (hipStream_t)stream;
-  hipError_t e = s.bf16 ? xattn::launch_score_bf16(s, Q, K, S, B, scores, workspace, hs)
-                        : xattn::launch_score_fp32(s, Q, K, S, B, scores, hs);
-  return hip_status(e, "xattn_score launch");
+  hipError_t e = s.bf16 ? xattn::launch_score_bf16(s, Q, K, S, B, phase, scores, workspace, hs)
+                        : xattn::launch_score_fp32(s, Q, K, S, B, phase, scores, hs);
+  return hip_status(e, what);
+}
+
+xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
+                         int32_t B, float* scores, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  xattn::PhaseMap antidiagonal{};
+  return run_score(shape, Q, K, S, B, antidiagonal, scores, workspace, workspace_bytes, stream,
+                   "xattn_score launch");
+}
+
+xattn_status xattn_score_pattern(const xattn_shape* shape, const void* Q, const void* K,
+                                 int32_t S, int32_t B, const int32_t* phase_host, float* scores,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!phase_host) return fail(XATTN_EINVAL, "phase_host must be non-NULL");
+  if (S < 1) return fail(XATTN_EINVAL, "S (%d) must be >= 1", S);
+  if (S > xattn::kMaxPhase)
+    return fail(XATTN_EUNSUPPORTED, "sampling patterns cover S <= %d, got %d", xattn::kMaxPhase, S);
+  xattn::PhaseMap ph{};
+  ph.custom = 1;
+  bool seen[xattn::kMaxPhase] = {};
+  for (int a = 0; a < S; ++a) {
+    const int32_t v = phase_host[a];
+    if (v < 0 || v >= S || seen[v])
+      return fail(XATTN_EINVAL, "phase is not a permutation of 0..%d (entry %d = %d)", S - 1, a, v);
+    seen[v] = true;
+    ph.v[a] = v;
+  }
+  return run_score(shape, Q, K, S, B, ph, scores, workspace, workspace_bytes, stream,
+                   "xattn_score_pattern launch");
 }
 
 xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* scores,

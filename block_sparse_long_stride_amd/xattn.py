@@ -17,7 +17,8 @@ XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EWORKSPACE, XATTN_EHIP = range
 XATTN_FP32, XATTN_BF16 = 0, 1
 
 # every entry point declared in include/xattn.h
-EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_select", "xattn_select_topk",
+EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_score_pattern", "xattn_select",
+           "xattn_select_topk",
            "xattn_select_topratio", "xattn_sparse_prefill", "xattn_full", "xattn_status_str",
            "xattn_last_error", "xattn_version")
 
@@ -50,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.xattn_score_workspace_bytes.restype = SZ
     L.xattn_score.argtypes = [SP, P, P, I32, I32, P, P, SZ, P]
     L.xattn_score.restype = I32
+    L.xattn_score_pattern.argtypes = [SP, P, P, I32, I32, P, P, P, SZ, P]
+    L.xattn_score_pattern.restype = I32
     L.xattn_select.argtypes = [I32, I32, I32, P, P, P, P, P, P]
     L.xattn_select.restype = I32
     L.xattn_select_topk.argtypes = [I32, I32, I32, P, I32, P, P, P, P]
@@ -113,9 +116,13 @@ def xattn_score_workspace_bytes(shape: Shape, S: int, B: int) -> int:
     return int(lib().xattn_score_workspace_bytes(ctypes.byref(shape), S, B))
 
 
-def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None, stream=None):
-    """Block scores, fp32 [hq][NB][NB]."""
+def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None, stream=None,
+                phase: Optional[Sequence[int]] = None):
+    """Block scores, fp32 [hq][NB][NB].  `phase` (a permutation of 0..S-1)
+    selects another sampling pattern through xattn_score_pattern; None is the
+    antidiagonal (xattn_score)."""
     torch = _torch()
+    import numpy as np
     sh = shape_of(Q, K, causal)
     NB = sh.L // B if B > 0 else 0
     if scores is None:
@@ -124,8 +131,17 @@ def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None,
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().xattn_score(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B, _ptr(scores),
-                             _ptr(workspace), ws_bytes, _stream(stream)), "xattn_score")
+    if phase is None:
+        _check(lib().xattn_score(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B, _ptr(scores),
+                                 _ptr(workspace), ws_bytes, _stream(stream)), "xattn_score")
+    else:
+        ph = np.ascontiguousarray(np.asarray(phase, dtype=np.int32))
+        if ph.shape != (S,):
+            raise ValueError(f"phase must hold S = {S} entries")
+        _check(lib().xattn_score_pattern(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B,
+                                         ph.ctypes.data_as(ctypes.c_void_p), _ptr(scores),
+                                         _ptr(workspace), ws_bytes, _stream(stream)),
+               "xattn_score_pattern")
     return scores
 
 

@@ -10,6 +10,7 @@
  *
  * Calls, in the order of the path:
  *   xattn_score          block scores from strided antidiagonal sums
+ *   xattn_score_pattern  block scores with another sampling pattern (ablation)
  *   xattn_select         threshold block selection -> mask, index lists
  *   xattn_select_topk    Top-K cut of the same ranking (selection ablation)
  *   xattn_select_topratio  Top-Ratio cut of the same ranking
@@ -85,6 +86,28 @@ size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t 
 xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
                          int32_t S, int32_t B, float* scores, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * Block scores with another sampling pattern inside each SxS tile: the
+ * pattern-geometry ablation (chapterpal.com Knowl 9, "Pattern Geometry":
+ * antidiagonal vs. diagonal vs. random sampling at the same stride;
+ * papercache.org summary, ablation "effectiveness of the antidiagonal
+ * pattern").  The pages name the patterns without defining them; here a
+ * pattern pairs query sub-row a of each reshaped row with key sub-row
+ * phase_host[a] of each reshaped column:
+ *   C[R][c] = sum_a <Q[R*S + a], K[c*S + phase_host[a]]>
+ * and everything after the product is as xattn_score.  phase_host[a] = S-1-a
+ * is xattn_score itself, phase_host[a] = a the diagonal pattern, a random
+ * permutation (drawn by the caller) the random pattern.
+ *
+ *   phase_host  in, HOST array of S int32: a permutation of 0 .. S-1
+ *               (else XATTN_EINVAL); S <= 64 (else XATTN_EUNSUPPORTED)
+ * Other arguments, workspace (xattn_score_workspace_bytes), outputs and
+ * errors as xattn_score.
+ */
+xattn_status xattn_score_pattern(const xattn_shape* shape, const void* Q, const void* K,
+                                 int32_t S, int32_t B, const int32_t* phase_host, float* scores,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Threshold block selection: find_blocks(A, tau) of section 2.2, per (head,

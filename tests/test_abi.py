@@ -76,6 +76,26 @@ def test_score_workspace_checks():
     assert lib.xattn_score_workspace_bytes(ctypes.byref(fp32), 16, 128) == 0
 
 
+def test_score_pattern_rejects():
+    lib = X.lib()
+    sh = _shape()
+
+    def call(ph, S=16):
+        arr = (ctypes.c_int32 * max(1, len(ph)))(*ph) if ph is not None else None
+        return lib.xattn_score_pattern(ctypes.byref(sh), DUMMY, DUMMY, S, 128, arr, DUMMY, DUMMY,
+                                       1 << 40, None)
+
+    assert call(None) == X.XATTN_EINVAL
+    assert call([0] * 16) == X.XATTN_EINVAL                          # repeated entry
+    assert call(list(range(15)) + [16]) == X.XATTN_EINVAL            # out of range
+    assert call(list(range(15)) + [-1]) == X.XATTN_EINVAL
+    assert b"permutation" in lib.xattn_last_error()
+    assert call(list(range(128)), S=128) == X.XATTN_EUNSUPPORTED     # S > 64
+    # a valid permutation still goes through the shape checks
+    sh.L = 4000
+    assert call(list(range(16))) == X.XATTN_EINVAL
+
+
 def test_select_rejects():
     lib = X.lib()
 

@@ -173,6 +173,27 @@ def test_fullsize_cut_rules_on_oracle_scores(fullsize):
                                           O.to_mask(sel, cfg.nb))
 
 
+def test_fullsize_pattern_scores(fullsize):
+    """Diagonal and random sampling patterns at full size: the sampled rows
+    against the oracle's pattern sums."""
+    from block_sparse_long_stride_amd import xattn_score
+    cfg, w, dev, r = fullsize
+    rng = np.random.default_rng(77 + cfg.cid)
+    for kind, ph in (("diagonal", list(range(cfg.S))),
+                     ("random", [int(x) for x in rng.permutation(cfg.S)])):
+        sc = xattn_score(dev["Q"], dev["K"], cfg.S, cfg.B, cfg.causal, phase=ph)
+        _sync()
+        rel = 0.0
+        for h in sorted({h for h, _ in r["pairs"]}):
+            qbs = [qb for hh, qb in r["pairs"] if hh == h]
+            want = O.block_scores(w.q64(h), w.k64(h // cfg.group), cfg.S, cfg.B, cfg.causal,
+                                  qblocks=qbs, phase=ph)
+            got = sc[h, qbs].cpu().numpy()
+            rel = max(rel, assert_scores_close(got, want, f"{kind} h{h}"))
+        del sc
+        print(f"[config {cfg.cid}] {kind} pattern: max rel score err {rel:.2e}")
+
+
 def test_fullsize_sparse_prefill(fullsize):
     """Sparse prefill on the oracle's selections of the sampled rows (other
     rows get empty lists) against oracle attention over the same blocks."""

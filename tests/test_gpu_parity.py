@@ -63,6 +63,36 @@ def test_scores_match_oracle(name):
     print(f"[{name}] max rel score err {rel:.2e}")
 
 
+def _phase(S, kind, seed=0):
+    if kind == "diagonal":
+        return list(range(S))
+    if kind == "antidiagonal":
+        return [S - 1 - a for a in range(S)]
+    return [int(x) for x in np.random.default_rng(seed).permutation(S)]
+
+
+@pytest.mark.parametrize("name", ["c1-fp32", "llm-S8-B128", "llm-S16-B128-offsets", "llm-bs4-S32",
+                                  "llm-d64-B64", "video-ragged", "noncausal-llm-fp32"])
+@pytest.mark.parametrize("kind", ["diagonal", "random", "antidiagonal"])
+def test_pattern_scores_match_oracle(name, kind):
+    """Sampling patterns of the pattern ablation through xattn_score_pattern
+    against the oracle's pattern sums (the antidiagonal map must reproduce
+    xattn_score bit for bit)."""
+    from block_sparse_long_stride_amd import xattn_score
+    cfg, w, dev, ora = case(name)
+    ph = _phase(cfg.S, kind, seed=cfg.S + 17)
+    print(f"[{name}] {kind} scores, phase {ph}", flush=True)
+    gpu = xattn_score(dev["Q"], dev["K"], cfg.S, cfg.B, cfg.causal, phase=ph)
+    _sync()
+    gpu = gpu.cpu().numpy()
+    want = np.stack([O.block_scores(w.q64(h), w.k64(h // cfg.group), cfg.S, cfg.B, cfg.causal,
+                                    phase=ph) for h in range(cfg.hq)])
+    rel = assert_scores_close(gpu, want)
+    print(f"[{name}] {kind}: max rel score err {rel:.2e}")
+    if kind == "antidiagonal":
+        np.testing.assert_array_equal(gpu, _gpu_scores(cfg, dev).cpu().numpy())
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_select_matches_oracle_on_same_scores(name):
     """Both sides rank the same fp32 scores: masks, idx and counts are exact."""
