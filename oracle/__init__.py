@@ -4,11 +4,13 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 bench's CPU-baseline leg, never by the library.
 """
 from .xattn_oracle import (Selection, antidiagonal_sums, approx_attention, block_mass,
-                           block_scores, block_sparse_attention, find_blocks,
+                           block_scores, block_sparse_attention, dit_attention, dit_run_density,
+                           dit_step_is_dense, find_blocks,
                            find_blocks_topk, find_blocks_topratio, full_attention, pattern_sums,
                            select_all, to_mask, topratio_count)
 
 __all__ = ["Selection", "antidiagonal_sums", "approx_attention", "block_mass",
-           "block_scores", "block_sparse_attention", "find_blocks", "find_blocks_topk",
+           "block_scores", "block_sparse_attention", "dit_attention", "dit_run_density",
+           "dit_step_is_dense", "find_blocks", "find_blocks_topk",
            "find_blocks_topratio", "full_attention", "pattern_sums", "select_all", "to_mask",
            "topratio_count"]

@@ -29,6 +29,8 @@ Readings where the pages are silent (each is pinned by a test):
   * sampling patterns other than the antidiagonal (named, not defined, in the
     pattern ablation): diagonal = key sub-row a for query sub-row a; random =
     a seeded permutation of the key sub-rows, drawn by the caller.
+  * the video warm-up: denoising steps count from 0; steps < warmup (5) run
+    dense attention, the rest the sparse path.
   * Top-K / Top-Ratio (the ablation's alternative cut rules, named but not
     defined on the pages): the same ranking as find_blocks, cut at a fixed
     count -- k blocks (K tokens / B), or the nearest integer to ratio * |valid|
@@ -260,3 +262,33 @@ def full_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, B: int, causal: 
     """Dense attention for the rows of query block qb (all keys, j <= i if causal)."""
     NB = Q.shape[0] // B
     return block_sparse_attention(Q, K, V, B, causal, qb, range(qb + 1 if causal else NB))
+
+
+# ---------------------------------------------------------------------------
+# Video DiT warm-up policy (chapterpal.com Knowl 4, "Full-Attention Denoising
+# Warmup"; papercache.org summary, video generation experiment): dense
+# attention for the first `warmup` denoising steps (5 of 50 on the pages),
+# XAttention afterwards.
+# ---------------------------------------------------------------------------
+def dit_step_is_dense(step: int, warmup: int = 5) -> bool:
+    """Denoising steps count from 0; steps 0 .. warmup-1 are dense."""
+    return step < warmup
+
+
+def dit_attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, S: int, B: int, tau: float,
+                  step: int, warmup: int, qb: int, causal: bool = False) -> np.ndarray:
+    """Output rows of query block qb at denoising step `step`: full attention
+    during the warm-up, else threshold-selected block-sparse attention."""
+    if dit_step_is_dense(step, warmup):
+        return full_attention(Q, K, V, B, causal, qb)
+    NB = Q.shape[0] // B
+    row = block_scores(Q, K, S, B, causal, qblocks=[qb])[0]
+    sel = find_blocks(row, qb + 1 if causal else NB, tau)
+    return block_sparse_attention(Q, K, V, B, causal, qb, sel.selected)
+
+
+def dit_run_density(sparse_density: float, steps: int = 50, warmup: int = 5) -> float:
+    """Share of attention blocks computed over a whole generation run: dense
+    steps count as density 1."""
+    n_dense = sum(1 for t in range(steps) if dit_step_is_dense(t, warmup))
+    return (n_dense + (steps - n_dense) * sparse_density) / steps

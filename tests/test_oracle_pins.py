@@ -436,3 +436,44 @@ def test_single_key_row_copies_value():
     np.testing.assert_allclose(out[0], V[8], rtol=0, atol=1e-15)
     # no selected block: rows output 0
     assert np.all(O.block_sparse_attention(Q, K, V, B, True, 1, []) == 0.0)
+
+
+# --- video DiT warm-up policy --------------------------------------------------
+def test_dit_schedule_first_five_of_fifty_dense():
+    dense = [t for t in range(50) if O.dit_step_is_dense(t, 5)]
+    assert dense == [0, 1, 2, 3, 4]
+    # density over the run: dense steps count as 1
+    assert math.isclose(O.dit_run_density(0.4, 50, 5), (5 + 45 * 0.4) / 50)
+    assert O.dit_run_density(1.0) == 1.0
+    assert O.dit_run_density(0.0, 50, 5) == 0.1
+    # sparsity over the run stays above 50% exactly when the sparse steps keep < 4/9 of blocks
+    assert O.dit_run_density(4 / 9 - 1e-9) < 0.5 < O.dit_run_density(4 / 9 + 1e-9)
+
+
+def test_dit_attention_dense_steps_and_tau_one_are_naive_attention():
+    rng = np.random.default_rng(21)
+    L, d, S, B = 32, 4, 2, 8
+    Q, K, V = (rng.standard_normal((L, d)) for _ in range(3))
+    naive = _naive_attention(Q, K, V, causal=False)
+    for qb in range(L // B):
+        rows = slice(qb * B, (qb + 1) * B)
+        for step in range(5):             # warm-up steps: dense whatever tau says
+            np.testing.assert_allclose(O.dit_attention(Q, K, V, S, B, 0.3, step, 5, qb),
+                                       naive[rows], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(O.dit_attention(Q, K, V, S, B, 1.0, 7, 5, qb), naive[rows],
+                                   rtol=0, atol=1e-12)
+
+
+def test_dit_attention_sparse_step_is_restricted_attention():
+    """After the warm-up, a query block attends to exactly the keys of its
+    selected blocks: equal to naive attention over those keys."""
+    rng = np.random.default_rng(22)
+    L, d, S, B = 32, 4, 2, 8
+    Q, K, V = (rng.standard_normal((L, d)) * 2 for _ in range(3))
+    sc = O.block_scores(Q, K, S, B, causal=False)
+    for qb in range(L // B):
+        sel = O.find_blocks(sc[qb], L // B, 0.6)
+        allowed = {j for kb in sel.selected for j in range(kb * B, (kb + 1) * B)}
+        want = _naive_attention(Q, K, V, causal=False, allowed=allowed)[qb * B:(qb + 1) * B]
+        np.testing.assert_allclose(O.dit_attention(Q, K, V, S, B, 0.6, 5, 5, qb), want,
+                                   rtol=0, atol=1e-12)
