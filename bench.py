@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     ap.add_argument("--no-next", action="store_true",
                     help="skip the measurements of the NEXT rows (selection cut rules ...)")
+    ap.add_argument("--no-dit", dest="next_dit", action="store_false",
+                    help="skip the video-DiT warm-up policy measurement (config 5)")
     ap.add_argument("--only", choices=["score", "select", "sparse", "full", "copy"],
                     help="profiling mode: run only this call `--steps` times (after one "
                          "untimed pass of the path), print nothing but a short summary; "
@@ -101,6 +103,50 @@ def cpu_baseline(cfg, w, seconds):
         rows += 1
     ms_full = spent / rows * cfg.hq * cfg.nb * 1e3
     return ms_full, rows, threads
+
+
+def dit_policy_rows(timed, stream, steps=50, warmup=5):
+    """Warm-up policy of the video-DiT experiment on the config-5 workload:
+    one dense (warm-up) step and one sparse step are timed; the 50-step run
+    is their weighted sum."""
+    import numpy as np
+    import torch
+    from block_sparse_long_stride_amd import xattn
+    from workloads import generate, get_config
+    cfg = get_config(5)
+    w = generate(cfg)
+    dev = "cuda"
+    Q, K, V = (torch.from_numpy(np.ascontiguousarray(getattr(w, k)).view(np.int16))
+               .view(torch.bfloat16).to(dev) for k in ("Q", "K", "V"))
+    out = torch.empty_like(Q)
+    sh = xattn.shape_of(Q, K, cfg.causal)
+    ws = torch.empty(xattn.xattn_dit_workspace_bytes(sh, cfg.S, cfg.B), dtype=torch.uint8,
+                     device=dev)
+    run = lambda t: xattn.xattn_dit_attention(Q, K, V, cfg.S, cfg.B, w.tau, step=t,
+                                              warmup_steps=warmup, causal=cfg.causal, out=out,
+                                              workspace=ws, stream=stream)
+    ms_dense = timed(lambda: run(0), reps=2)
+    ms_sparse = timed(lambda: run(warmup), reps=2)
+    NB = cfg.L // cfg.B
+    counts = ws[xattn_counts_offset(ws.numel(), cfg.hq, NB):].view(torch.int32)[:cfg.hq * NB]
+    dens = int(counts.to(torch.int64).sum()) / (cfg.hq * NB * NB)
+    n_dense = sum(1 for t in range(steps) if t < warmup)
+    total = n_dense * ms_dense + (steps - n_dense) * ms_sparse
+    res = {"workload": f"config5 {cfg.name}: L={cfg.L}, hq=hkv={cfg.hq}, d={cfg.d}, bf16, "
+                       f"non-causal, S={cfg.S}, B={cfg.B}, tau={cfg.tau}",
+           "steps": steps, "warmup_steps": warmup, "dense_step_ms": round(ms_dense, 3),
+           "sparse_step_ms": round(ms_sparse, 3), "sparse_step_density": round(dens, 5),
+           "run_ms_from_step_times": round(total, 1),
+           "run_ms_all_dense": round(steps * ms_dense, 1),
+           "run_density": round((n_dense + (steps - n_dense) * dens) / steps, 5)}
+    del Q, K, V, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def xattn_counts_offset(ws_bytes, hq, NB):
+    """Byte offset of the counts array at the end of the DiT workspace."""
+    return ws_bytes - (hq * NB * 4 + 255) // 256 * 256
 
 
 def main():
@@ -268,6 +314,17 @@ def main():
                 "frac_bf16_peak": round(F_score / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "density_threshold_select": round(n_p / valid, 5)}
         xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores, workspace=ws, stream=stream)
+        # fused scoring + selection against the two calls, same workload
+        if cfg.dtype == "bf16":
+            ms_f = timed(lambda: xattn.xattn_score_select(Q, K, cfg.S, cfg.B, w.tau, cfg.causal,
+                                                          mask=mask, idx=idx, counts=counts,
+                                                          workspace=ws, stream=stream))
+            next_rows["f2_score_select_fused"] = {
+                "ms": round(ms_f, 3), "two_calls_ms": round(score_ms + select_ms, 3),
+                "density": round(int(counts.to(torch.int64).sum()) / valid, 5)}
+        # video-DiT warm-up policy on the config-5 workload (non-causal video tokens)
+        if args.next_dit:
+            next_rows["f2_dit_policy"] = dit_policy_rows(timed, stream)
         # restore the threshold selection for anything that follows
         xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
                            stream=stream)

@@ -40,6 +40,12 @@ struct TauArray {
 };
 hipError_t launch_select(int hq, int NB, int causal, const float* scores, const TauArray& tau,
                          uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
+// Scoring GEMM, then finishing and threshold selection fused in one kernel
+// (no score matrix in memory); antidiagonal pattern, bf16 inputs.  ws as for
+// launch_score_bf16.
+hipError_t launch_score_select_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
+                                    const TauArray& tau, uint64_t* mask, int32_t* idx,
+                                    int32_t* counts, void* ws, hipStream_t st);
 // Fixed-count cut rules on the same ranking: Top-K (k blocks) and Top-Ratio
 // (the nearest integer to ratio * valid blocks), both clamped to [1, valid].
 hipError_t launch_select_topk(int hq, int NB, int causal, const float* scores, int k_blocks,

@@ -25,6 +25,7 @@
 // adds the B/S rows of each query block and divides by B/S.
 #include "common.h"
 #include "launch.h"
+#include "select_row.h"
 
 namespace xattn {
 namespace {
@@ -299,6 +300,52 @@ struct FixupParams {
   int hq, NB, Lr, nR32, nct, bs, causal;
 };
 
+// Softmax statistics of reshaped row R (index r within its 32-row group) from
+// the 64-column range snapshots M, Z of that group: the row max and 1 / the
+// row denominator.  Eight consecutive lanes share a row (sub = lane & 7) and
+// combine their partial results with xor shuffles, so every caller computes
+// bit-identical values; a whole aligned 8-lane group always calls together.
+__device__ __forceinline__ void row_stats(const float* M, const float* Z, int r, int R, int Lr,
+                                          int nct, int bs, int causal, int sub, float& m_out,
+                                          float& invz_out) {
+  int nct_r = nct;
+  if (causal) {
+    const int last = (R / bs + 1) * bs - 1;   // last row of R's query block
+    nct_r = min(nct, last / kWaveCols + 1);
+  }
+  float m = -INFINITY;
+  if (R < Lr)
+    for (int c = sub; c < nct_r; c += 8) m = fmaxf(m, M[c * 32 + r]);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float z = 0.f;
+  if (R < Lr && m != -INFINITY)
+    for (int c = sub; c < nct_r; c += 8) {
+      const float mc = M[c * 32 + r];
+      if (mc != -INFINITY) z += Z[c * 32 + r] * fast_exp2(mc - m);
+    }
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) z += __shfl_xor(z, o);
+  m_out = m;
+  invz_out = (z > 0.f) ? 1.0f / z : 0.f;
+}
+
+// Block score of key block kb for the query block whose reshaped rows are
+// r0 .. r0+bs-1 of the group: the rows' partial block sums rescaled to the
+// rows' final softmax, summed in row order, divided by bs.
+__device__ __forceinline__ float block_score(const float* P, const float* M, const float* s_mfin,
+                                             const float* s_invz, int kb, int r0, int bs,
+                                             float inv_bs) {
+  const int c = (kb * bs) / kWaveCols;
+  float acc = 0.f;
+  for (int r = r0; r < r0 + bs; ++r) {
+    const float mc = M[c * 32 + r];
+    if (mc == -INFINITY) continue;
+    acc += P[(size_t)kb * 32 + r] * fast_exp2(mc - s_mfin[r]) * s_invz[r];
+  }
+  return acc * inv_bs;
+}
+
 // One workgroup per (head, 32 reshaped rows).
 __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   __shared__ float s_mfin[32];
@@ -314,28 +361,11 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   // 1. per row: softmax max and denominator from the range snapshots
   {
     const int r = tid >> 3, sub = tid & 7;
-    const int R = rg * 32 + r;
-    int nct_r = p.nct;
-    if (p.causal) {
-      const int last = (R / p.bs + 1) * p.bs - 1;   // last row of R's query block
-      nct_r = min(p.nct, last / kWaveCols + 1);
-    }
-    float m = -INFINITY;
-    if (R < p.Lr)
-      for (int c = sub; c < nct_r; c += 8) m = fmaxf(m, M[c * 32 + r]);
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float z = 0.f;
-    if (R < p.Lr && m != -INFINITY)
-      for (int c = sub; c < nct_r; c += 8) {
-        const float mc = M[c * 32 + r];
-        if (mc != -INFINITY) z += Z[c * 32 + r] * fast_exp2(mc - m);
-      }
-#pragma unroll
-    for (int o = 1; o < 8; o <<= 1) z += __shfl_xor(z, o);
+    float m, invz;
+    row_stats(M, Z, r, rg * 32 + r, p.Lr, p.nct, p.bs, p.causal, sub, m, invz);
     if (sub == 0) {
       s_mfin[r] = m;
-      s_invz[r] = (z > 0.f) ? 1.0f / z : 0.f;
+      s_invz[r] = invz;
     }
   }
   __syncthreads();
@@ -348,19 +378,65 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
     const int kb = it / nq, q = it % nq;
     const int qb = qb0 + q;
     if (qb >= p.NB) continue;
-    float out = 0.f;
-    if (!p.causal || kb <= qb) {
-      const int c = (kb * p.bs) / kWaveCols;
-      float acc = 0.f;
-      for (int r = q * p.bs; r < (q + 1) * p.bs; ++r) {
-        const float mc = M[c * 32 + r];
-        if (mc == -INFINITY) continue;
-        acc += P[(size_t)kb * 32 + r] * fast_exp2(mc - s_mfin[r]) * s_invz[r];
-      }
-      out = acc * inv_bs;
-    }
+    const float out = (!p.causal || kb <= qb)
+                          ? block_score(P, M, s_mfin, s_invz, kb, q * p.bs, p.bs, inv_bs) : 0.f;
     p.scores[((size_t)h * p.NB + qb) * p.NB + kb] = out;
   }
+}
+
+// Fused finishing + threshold selection: one workgroup per (head, query
+// block) computes the block scores of its row exactly as score_fixup does --
+// same helpers, same order, so the same bits -- keeps them in LDS and ranks
+// and cuts them (rank_and_cut, as xattn_select).  The [hq][NB][NB] score
+// matrix never reaches memory.
+struct FusedParams {
+  const float* P;
+  const float* M;
+  const float* Z;
+  uint64_t* mask;
+  int32_t* idx;
+  int32_t* counts;
+  int NB, Lr, nR32, nct, bs, causal, nwords;
+  TauArray tau;
+};
+
+template <int CAP>
+__global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams p) {
+  __shared__ SelectScratch<CAP> sh;
+  __shared__ float s_row[CAP];
+  __shared__ float s_mfin[32];
+  __shared__ float s_invz[32];
+  const int row = blockIdx.x;
+  const int h = row / p.NB, qb = row % p.NB;
+  const int tid = threadIdx.x;
+  const int R0 = qb * p.bs, rg = R0 / 32, r0 = R0 % 32;
+  const size_t rowbase = (size_t)h * p.nR32 + rg;
+  const float* M = p.M + rowbase * p.nct * 32;
+  const float* Z = p.Z + rowbase * p.nct * 32;
+  const float* P = p.P + rowbase * p.NB * 32;
+  {
+    // rows r0 .. r0+bs-1 of the group, 8 lanes each (lanes past bs rows idle
+    // through the same code on a row past Lr)
+    const int rl = tid >> 3, sub = tid & 7;
+    const bool used = rl < p.bs;
+    const int r = r0 + (used ? rl : 0);
+    float m, invz;
+    row_stats(M, Z, r, used ? rg * 32 + r : p.Lr, p.Lr, p.nct, p.bs, p.causal, sub, m, invz);
+    if (used && sub == 0) {
+      s_mfin[r] = m;
+      s_invz[r] = invz;
+    }
+  }
+  __syncthreads();
+  const float inv_bs = 1.0f / (float)p.bs;
+  for (int kb = tid; kb < p.NB; kb += kSelectThreads)
+    s_row[kb] = (!p.causal || kb <= qb) ? block_score(P, M, s_mfin, s_invz, kb, r0, p.bs, inv_bs)
+                                        : 0.f;
+  __syncthreads();
+  const CutSpec cut{kThreshold, 0, 0.f, p.tau.v[h]};
+  rank_and_cut<CAP>(sh, [&](int i) { return s_row[i]; }, p.causal ? qb + 1 : p.NB, p.NB,
+                    p.nwords, cut, p.mask + (size_t)row * p.nwords, p.idx + (size_t)row * p.NB,
+                    p.counts + row);
 }
 
 template <int D, int BS>
@@ -404,13 +480,14 @@ size_t score_workspace_bytes(const Shape& s, int S, int B) {
   return (w.p_elems + 2 * w.m_elems) * sizeof(float);
 }
 
-hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
-                             const PhaseMap& phase, float* scores, void* ws, hipStream_t st) {
-  const WsLayout wl = ws_layout(s, S, B);
+namespace {
+
+// The scoring GEMM into the workspace partials (P, M, Z).
+hipError_t run_score_gemm(const Shape& s, const void* Q, const void* K, int S, int B,
+                          const PhaseMap& phase, void* ws, const WsLayout& wl, hipStream_t st) {
   float* P = (float*)ws;
   float* M = P + wl.p_elems;
   float* Z = M + wl.m_elems;
-
   GemmParams gp;
   gp.Q = (const uint16_t*)Q;
   gp.K = (const uint16_t*)K;
@@ -433,23 +510,64 @@ hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S
   gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
   gp.phase = phase;
   const int bs = B / S;
-  hipError_t e = (s.d == 128) ? launch_gemm_bs<128>(gp, bs, st) : launch_gemm_bs<64>(gp, bs, st);
-  if (e != hipSuccess) return e;
+  return (s.d == 128) ? launch_gemm_bs<128>(gp, bs, st) : launch_gemm_bs<64>(gp, bs, st);
+}
 
+template <int CAP>
+hipError_t launch_fused(const FusedParams& fp, int rows, hipStream_t st) {
+  hipLaunchKernelGGL((score_select_fused<CAP>), dim3(rows), dim3(kSelectThreads), 0, st, fp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
+                             const PhaseMap& phase, float* scores, void* ws, hipStream_t st) {
+  const WsLayout wl = ws_layout(s, S, B);
+  hipError_t e = run_score_gemm(s, Q, K, S, B, phase, ws, wl, st);
+  if (e != hipSuccess) return e;
   FixupParams fp;
-  fp.P = P;
-  fp.M = M;
-  fp.Z = Z;
+  fp.P = (float*)ws;
+  fp.M = fp.P + wl.p_elems;
+  fp.Z = fp.M + wl.m_elems;
   fp.scores = scores;
   fp.hq = s.hq;
   fp.NB = wl.NB;
   fp.Lr = wl.Lr;
   fp.nR32 = wl.nR32;
   fp.nct = wl.nct;
-  fp.bs = bs;
+  fp.bs = B / S;
   fp.causal = s.causal;
   hipLaunchKernelGGL(score_fixup, dim3(s.hq * wl.nR32), dim3(256), 0, st, fp);
   return hipGetLastError();
+}
+
+hipError_t launch_score_select_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
+                                    const TauArray& tau, uint64_t* mask, int32_t* idx,
+                                    int32_t* counts, void* ws, hipStream_t st) {
+  const WsLayout wl = ws_layout(s, S, B);
+  PhaseMap antidiagonal{};
+  hipError_t e = run_score_gemm(s, Q, K, S, B, antidiagonal, ws, wl, st);
+  if (e != hipSuccess) return e;
+  FusedParams fp;
+  fp.P = (float*)ws;
+  fp.M = fp.P + wl.p_elems;
+  fp.Z = fp.M + wl.m_elems;
+  fp.mask = mask;
+  fp.idx = idx;
+  fp.counts = counts;
+  fp.NB = wl.NB;
+  fp.Lr = wl.Lr;
+  fp.nR32 = wl.nR32;
+  fp.nct = wl.nct;
+  fp.bs = B / S;
+  fp.causal = s.causal;
+  fp.nwords = (wl.NB + 63) / 64;
+  fp.tau = tau;
+  const int rows = s.hq * wl.NB;
+  if (wl.NB <= 256) return launch_fused<256>(fp, rows, st);
+  if (wl.NB <= 1024) return launch_fused<1024>(fp, rows, st);
+  return launch_fused<4096>(fp, rows, st);
 }
 
 }  // namespace xattn

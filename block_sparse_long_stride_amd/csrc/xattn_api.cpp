@@ -252,6 +252,111 @@ xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K, 
   return hip_status(e, "xattn_full launch");
 }
 
+// ---- fused scoring + selection, and the video-DiT warm-up policy ----------
+
+static xattn_status check_tau(int32_t hq, const float* tau_host, xattn::TauArray* tau) {
+  if (!tau_host) return fail(XATTN_EINVAL, "tau_host must be non-NULL");
+  if (hq > xattn::kMaxHeads)
+    return fail(XATTN_EUNSUPPORTED, "selection covers hq <= %d, got %d", xattn::kMaxHeads, hq);
+  for (int h = 0; h < xattn::kMaxHeads; ++h) tau->v[h] = 1.0f;
+  for (int h = 0; h < hq; ++h) {
+    const float t = tau_host[h];
+    if (!(t > 0.0f && t <= 1.0f))
+      return fail(XATTN_EINVAL, "tau[%d] = %g is outside (0, 1]", h, (double)t);
+    tau->v[h] = t;
+  }
+  return XATTN_OK;
+}
+
+// Validation shared by the fused path and the warm-up policy's sparse steps.
+static xattn_status check_fused_args(const xattn_shape* shape, int32_t S, int32_t B,
+                                     const float* tau_host, xattn::Shape* s,
+                                     xattn::TauArray* tau) {
+  xattn_status st = check_score_args(shape, S, B, s);
+  if (st != XATTN_OK) return st;
+  if (!s->bf16) return fail(XATTN_EUNSUPPORTED, "the fused scoring + selection path is bf16 only");
+  const int NB = s->L / B;
+  if (NB > xattn::kMaxSelectBlocks)
+    return fail(XATTN_EUNSUPPORTED, "selection covers NB <= %d, got %d", xattn::kMaxSelectBlocks, NB);
+  return check_tau(s->hq, tau_host, tau);
+}
+
+xattn_status xattn_score_select(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
+                                int32_t B, const float* tau_host, uint64_t* mask, int32_t* idx,
+                                int32_t* counts, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  xattn::Shape s;
+  xattn::TauArray tau;
+  xattn_status st = check_fused_args(shape, S, B, tau_host, &s, &tau);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !mask || !idx || !counts)
+    return fail(XATTN_EINVAL, "Q, K, mask, idx and counts must be non-NULL");
+  const size_t need = xattn::score_workspace_bytes(s, S, B);
+  if (!workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+  if (workspace_bytes < need)
+    return fail(XATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  hipError_t e = xattn::launch_score_select_bf16(s, Q, K, S, B, tau, mask, idx, counts, workspace,
+                                                 (hipStream_t)stream);
+  return hip_status(e, "xattn_score_select launch");
+}
+
+namespace {
+struct DitLayout {
+  size_t score, mask, idx, counts, total;
+};
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+DitLayout dit_layout(const xattn::Shape& s, int S, int B) {
+  const size_t NB = (size_t)(s.L / B), rows = (size_t)s.hq * NB;
+  DitLayout d;
+  d.score = 0;
+  d.mask = align_up(xattn::score_workspace_bytes(s, S, B));
+  d.idx = d.mask + align_up(rows * ((NB + 63) / 64) * 8);
+  d.counts = d.idx + align_up(rows * NB * 4);
+  d.total = d.counts + align_up(rows * 4);
+  return d;
+}
+}  // namespace
+
+size_t xattn_dit_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t B) {
+  xattn::Shape s;
+  std::string saved = g_last_error;
+  if (check_score_args(shape, S, B, &s) != XATTN_OK) {
+    g_last_error = saved;
+    return 0;
+  }
+  return dit_layout(s, S, B).total;
+}
+
+xattn_status xattn_dit_attention(const xattn_shape* shape, const void* Q, const void* K,
+                                 const void* V, int32_t S, int32_t B, const float* tau_host,
+                                 int32_t step, int32_t warmup_steps, void* O, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (step < 0 || warmup_steps < 0)
+    return fail(XATTN_EINVAL, "step (%d) and warmup_steps (%d) must be >= 0", step, warmup_steps);
+  if (step < warmup_steps) return xattn_full(shape, Q, K, V, O, stream);   // warm-up: dense
+  xattn::Shape s;
+  xattn::TauArray tau;
+  xattn_status st = check_fused_args(shape, S, B, tau_host, &s, &tau);
+  if (st != XATTN_OK) return st;
+  st = check_attn_args(s, B);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !V || !O) return fail(XATTN_EINVAL, "Q, K, V and O must be non-NULL");
+  const DitLayout d = dit_layout(s, S, B);
+  if (!workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", d.total);
+  if (workspace_bytes < d.total)
+    return fail(XATTN_EWORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, d.total);
+  char* ws = (char*)workspace;
+  uint64_t* mask = (uint64_t*)(ws + d.mask);
+  int32_t* idx = (int32_t*)(ws + d.idx);
+  int32_t* counts = (int32_t*)(ws + d.counts);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e = xattn::launch_score_select_bf16(s, Q, K, S, B, tau, mask, idx, counts, ws, hs);
+  if (e != hipSuccess) return hip_status(e, "xattn_dit_attention scoring launch");
+  e = xattn::launch_flash_bf16(s, Q, K, V, B, idx, counts, O, hs);
+  return hip_status(e, "xattn_dit_attention attention launch");
+}
+
 const char* xattn_status_str(xattn_status status) {
   switch (status) {
     case XATTN_OK: return "ok";

@@ -19,7 +19,8 @@ XATTN_FP32, XATTN_BF16 = 0, 1
 # every entry point declared in include/xattn.h
 EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_score_pattern", "xattn_select",
            "xattn_select_topk",
-           "xattn_select_topratio", "xattn_sparse_prefill", "xattn_full", "xattn_status_str",
+           "xattn_select_topratio", "xattn_score_select", "xattn_sparse_prefill", "xattn_full",
+           "xattn_dit_workspace_bytes", "xattn_dit_attention", "xattn_status_str",
            "xattn_last_error", "xattn_version")
 
 
@@ -59,6 +60,12 @@ def lib() -> ctypes.CDLL:
     L.xattn_select_topk.restype = I32
     L.xattn_select_topratio.argtypes = [I32, I32, I32, P, ctypes.c_float, P, P, P, P]
     L.xattn_select_topratio.restype = I32
+    L.xattn_score_select.argtypes = [SP, P, P, I32, I32, P, P, P, P, P, SZ, P]
+    L.xattn_score_select.restype = I32
+    L.xattn_dit_workspace_bytes.argtypes = [SP, I32, I32]
+    L.xattn_dit_workspace_bytes.restype = SZ
+    L.xattn_dit_attention.argtypes = [SP, P, P, P, I32, I32, P, I32, I32, P, P, SZ, P]
+    L.xattn_dit_attention.restype = I32
     L.xattn_sparse_prefill.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.xattn_sparse_prefill.restype = I32
     L.xattn_full.argtypes = [SP, P, P, P, P, P]
@@ -200,6 +207,62 @@ def xattn_select_topratio(scores, ratio: float, causal: bool, mask=None, idx=Non
                                        _ptr(mask), _ptr(idx), _ptr(counts), _stream(stream)),
            "xattn_select_topratio")
     return mask, idx, counts
+
+
+def _tau_host(tau, hq):
+    import numpy as np
+    return np.ascontiguousarray(np.broadcast_to(np.asarray(tau, dtype=np.float32), (hq,)))
+
+
+def xattn_score_select(Q, K, S: int, B: int, tau: Sequence[float], causal: bool, mask=None,
+                       idx=None, counts=None, workspace=None, stream=None) -> Tuple:
+    """Fused scoring + threshold selection (no score matrix): (mask, idx, counts)."""
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    NB = sh.L // B if B > 0 else 0
+    words = (NB + 63) // 64
+    if mask is None:
+        mask = torch.empty((sh.hq, NB, words), dtype=torch.int64, device=Q.device)
+    if idx is None:
+        idx = torch.empty((sh.hq, NB, NB), dtype=torch.int32, device=Q.device)
+    if counts is None:
+        counts = torch.empty((sh.hq, NB), dtype=torch.int32, device=Q.device)
+    need = xattn_score_workspace_bytes(sh, S, B)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    t = _tau_host(tau, sh.hq)
+    _check(lib().xattn_score_select(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B,
+                                    t.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(idx),
+                                    _ptr(counts), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "xattn_score_select")
+    return mask, idx, counts
+
+
+def xattn_dit_workspace_bytes(sh: Shape, S: int, B: int) -> int:
+    return int(lib().xattn_dit_workspace_bytes(ctypes.byref(sh), S, B))
+
+
+def xattn_dit_attention(Q, K, V, S: int, B: int, tau: Sequence[float], step: int,
+                        warmup_steps: int = 5, causal: bool = False, out=None, workspace=None,
+                        stream=None):
+    """One denoising step's attention under the full-attention warm-up policy."""
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
+        raise ValueError("V must match K")
+    if out is None:
+        out = torch.empty_like(Q)
+    if workspace is None and step >= warmup_steps:
+        workspace = torch.empty(max(xattn_dit_workspace_bytes(sh, S, B), 1), dtype=torch.uint8,
+                                device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    t = _tau_host(tau, sh.hq)
+    _check(lib().xattn_dit_attention(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), S, B,
+                                     t.ctypes.data_as(ctypes.c_void_p), int(step),
+                                     int(warmup_steps), _ptr(out), _ptr(workspace), ws_bytes,
+                                     _stream(stream)), "xattn_dit_attention")
+    return out
 
 
 def xattn_sparse_prefill(Q, K, V, B: int, idx, counts, causal: bool, out=None, stream=None):

@@ -14,7 +14,9 @@
  *   xattn_select         threshold block selection -> mask, index lists
  *   xattn_select_topk    Top-K cut of the same ranking (selection ablation)
  *   xattn_select_topratio  Top-Ratio cut of the same ranking
+ *   xattn_score_select   scoring + threshold selection fused (no score matrix)
  *   xattn_sparse_prefill attention over the selected blocks
+ *   xattn_dit_attention  dense warm-up steps, then the sparse path (video DiT)
  *   xattn_full           dense attention (the speed baseline)
  *
  * Conventions for every call:
@@ -148,6 +150,42 @@ xattn_status xattn_select_topk(int32_t hq, int32_t NB, int32_t causal, const flo
 xattn_status xattn_select_topratio(int32_t hq, int32_t NB, int32_t causal, const float* scores,
                                    float ratio, uint64_t* mask, int32_t* idx, int32_t* counts,
                                    void* stream);
+
+/*
+ * Fused scoring + threshold selection: xattn_score followed by xattn_select
+ * (tau per head, antidiagonal pattern) in one call whose block scores never
+ * reach memory -- the per-query-block finishing of the scores and the
+ * ranking/cut run in one kernel.  Results are bit-identical to the two calls.
+ * bf16 only (fp32: XATTN_EUNSUPPORTED).  The workspace is
+ * xattn_score_workspace_bytes(shape, S, B) bytes; arguments, outputs and
+ * errors otherwise as xattn_score and xattn_select.
+ */
+xattn_status xattn_score_select(const xattn_shape* shape, const void* Q, const void* K, int32_t S,
+                                int32_t B, const float* tau_host, uint64_t* mask, int32_t* idx,
+                                int32_t* counts, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Attention of one layer at one denoising step of a video diffusion
+ * transformer under the full-attention warm-up policy (chapterpal.com
+ * Knowl 4, "Full-Attention Denoising Warmup"; papercache.org summary, video
+ * generation experiment): steps 0 .. warmup_steps-1 (the pages: the first 5
+ * of 50) run dense attention (xattn_full); later steps run
+ * xattn_score_select with tau_host and then xattn_sparse_prefill.
+ *
+ *   step, warmup_steps  >= 0 (else XATTN_EINVAL); step counts from 0
+ *   workspace           device, xattn_dit_workspace_bytes(shape, S, B) bytes:
+ *                       scoring partials, then mask, idx and counts of the
+ *                       selection (left there after a sparse step); unused
+ *                       (may be NULL) on warm-up steps
+ * Other arguments and errors as xattn_full / xattn_score_select /
+ * xattn_sparse_prefill (bf16 only on sparse steps).
+ */
+size_t xattn_dit_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t B);
+xattn_status xattn_dit_attention(const xattn_shape* shape, const void* Q, const void* K,
+                                 const void* V, int32_t S, int32_t B, const float* tau_host,
+                                 int32_t step, int32_t warmup_steps, void* O, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse attention (section 1, step 3): for query block qb of head h,

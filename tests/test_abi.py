@@ -96,6 +96,32 @@ def test_score_pattern_rejects():
     assert call(list(range(16))) == X.XATTN_EINVAL
 
 
+def test_fused_and_dit_reject():
+    lib = X.lib()
+    sh = _shape()
+    tau = np.full(4, 0.9, dtype=np.float32)
+    tp = tau.ctypes.data_as(ctypes.c_void_p)
+    need = lib.xattn_score_workspace_bytes(ctypes.byref(sh), 16, 128)
+    fused = lambda **kw: lib.xattn_score_select(
+        ctypes.byref(kw.get("sh", sh)), DUMMY, DUMMY, 16, 128, kw.get("tau", tp), DUMMY, DUMMY,
+        DUMMY, kw.get("ws", DUMMY), kw.get("bytes", need), None)
+    assert fused(bytes=need - 1) == X.XATTN_EWORKSPACE
+    assert fused(ws=None) == X.XATTN_EINVAL
+    assert fused(tau=None) == X.XATTN_EINVAL
+    bad = np.array([0.9, 0.9, 1.5, 0.9], dtype=np.float32)
+    assert fused(tau=bad.ctypes.data_as(ctypes.c_void_p)) == X.XATTN_EINVAL
+    assert fused(sh=_shape(dtype=X.XATTN_FP32)) == X.XATTN_EUNSUPPORTED
+    dneed = lib.xattn_dit_workspace_bytes(ctypes.byref(sh), 16, 128)
+    assert dneed > need
+    dit = lambda step, warm=5, bytes=dneed, ws=DUMMY: lib.xattn_dit_attention(
+        ctypes.byref(sh), DUMMY, DUMMY, DUMMY, 16, 128, tp, step, warm, DUMMY, ws, bytes, None)
+    assert dit(-1) == X.XATTN_EINVAL
+    assert dit(7, warm=-2) == X.XATTN_EINVAL
+    assert dit(7, bytes=dneed - 1) == X.XATTN_EWORKSPACE
+    assert dit(7, ws=None) == X.XATTN_EINVAL
+    assert lib.xattn_dit_workspace_bytes(ctypes.byref(_shape(L=4000)), 16, 128) == 0
+
+
 def test_select_rejects():
     lib = X.lib()
 

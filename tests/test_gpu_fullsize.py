@@ -194,6 +194,23 @@ def test_fullsize_pattern_scores(fullsize):
         print(f"[config {cfg.cid}] {kind} pattern: max rel score err {rel:.2e}")
 
 
+def test_fullsize_fused_score_select(fullsize):
+    """The fused scoring + selection path equals the two-call path bit for bit
+    on the sampled rows (bf16 configs)."""
+    from block_sparse_long_stride_amd import xattn_score_select
+    cfg, w, dev, r = fullsize
+    if cfg.dtype != "bf16":
+        pytest.skip("the fused path is bf16 only")
+    mask, idx, counts = xattn_score_select(dev["Q"], dev["K"], cfg.S, cfg.B, w.tau, cfg.causal)
+    _sync()
+    for key in r["pairs"]:
+        assert int(counts[key[0], key[1]]) == r["counts"][key]
+        np.testing.assert_array_equal(idx[key[0], key[1]].cpu().numpy(), r["idx"][key])
+        np.testing.assert_array_equal(mask[key[0], key[1]].cpu().numpy().view(np.uint64),
+                                      r["mask"][key])
+    del mask, idx, counts
+
+
 def test_fullsize_sparse_prefill(fullsize):
     """Sparse prefill on the oracle's selections of the sampled rows (other
     rows get empty lists) against oracle attention over the same blocks."""

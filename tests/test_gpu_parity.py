@@ -290,3 +290,59 @@ def test_sparse_prefill_edge_lists(name):
             want[h, qb * cfg.B:(qb + 1) * cfg.B] = O.block_sparse_attention(
                 q, k, v, cfg.B, cfg.causal, qb, expect_lists[(h, qb)])
     assert_outputs_close(got, want, cfg.dtype)
+
+
+BF16 = [n for n, c in SMALL.items() if c.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("name", BF16)
+def test_fused_score_select_equals_two_calls(name):
+    """xattn_score_select (finishing + selection in one kernel) gives the same
+    mask, idx and counts, bit for bit, as xattn_score then xattn_select."""
+    from block_sparse_long_stride_amd import xattn_score_select, xattn_select
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] fused score+select", flush=True)
+    sc = _gpu_scores(cfg, dev)
+    m1, i1, c1 = xattn_select(sc, w.tau, cfg.causal)
+    m2, i2, c2 = xattn_score_select(dev["Q"], dev["K"], cfg.S, cfg.B, w.tau, cfg.causal)
+    _sync()
+    for a, b in ((m1, m2), (i1, i2), (c1, c2)):
+        np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+@pytest.mark.parametrize("name", ["video-ragged", "llm-S8-B128", "llm-d64-B64"])
+def test_dit_attention_policy(name):
+    """Warm-up steps run dense attention (bit-identical to xattn_full); later
+    steps run the fused selection and sparse prefill (bit-identical to those
+    calls), and match the oracle's policy output."""
+    import torch
+    from block_sparse_long_stride_amd import (xattn_dit_attention, xattn_full, xattn_score_select,
+                                              xattn_sparse_prefill)
+    cfg, w, dev, ora = case(name)
+    print(f"[{name}] dit policy", flush=True)
+    warm = xattn_dit_attention(dev["Q"], dev["K"], dev["V"], cfg.S, cfg.B, w.tau, step=4,
+                               warmup_steps=5, causal=cfg.causal)
+    full = xattn_full(dev["Q"], dev["K"], dev["V"], cfg.causal)
+    sparse = xattn_dit_attention(dev["Q"], dev["K"], dev["V"], cfg.S, cfg.B, w.tau, step=5,
+                                 warmup_steps=5, causal=cfg.causal)
+    _, idx, counts = xattn_score_select(dev["Q"], dev["K"], cfg.S, cfg.B, w.tau, cfg.causal)
+    ref = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx, counts, cfg.causal)
+    _sync()
+    np.testing.assert_array_equal(out_to_f64(warm), out_to_f64(full))
+    np.testing.assert_array_equal(out_to_f64(sparse), out_to_f64(ref))
+    # against the oracle: dense rows exactly as full attention; sparse rows on the
+    # GPU's own selection (isolates the attention from the tau band)
+    got_w, got_s = out_to_f64(warm), out_to_f64(sparse)
+    idx_np, cnt_np = idx.cpu().numpy(), counts.cpu().numpy()
+    want_w, want_s = np.zeros_like(got_w), np.zeros_like(got_s)
+    for h in range(cfg.hq):
+        g = h // cfg.group
+        q, k, v = w.q64(h), w.k64(g), w.v64(g)
+        for qb in range(cfg.nb):
+            rows = slice(qb * cfg.B, (qb + 1) * cfg.B)
+            want_w[h, rows] = O.dit_attention(q, k, v, cfg.S, cfg.B, float(w.tau[h]), 4, 5, qb,
+                                              cfg.causal)
+            want_s[h, rows] = O.block_sparse_attention(q, k, v, cfg.B, cfg.causal, qb,
+                                                       idx_np[h, qb, :cnt_np[h, qb]])
+    assert_outputs_close(got_w, want_w, cfg.dtype)
+    assert_outputs_close(got_s, want_s, cfg.dtype)
