@@ -31,6 +31,11 @@ Readings where the pages are silent (each is pinned by a test):
     a seeded permutation of the key sub-rows, drawn by the caller.
   * the video warm-up: denoising steps count from 0; steps < warmup (5) run
     dense attention, the rest the sparse path.
+  * threshold prediction: each head takes k = 0 .. R reduction steps (x0.9
+    each) and exactly M steps are distributed; the garbled recurrence is read
+    as the 0/1 (R = 1) or multiple-choice selection DP; the performance proxy
+    is minus the summed relative squared output error (parity unpinned against
+    the pages' accuracy numbers, which need a trained model).
   * Top-K / Top-Ratio (the ablation's alternative cut rules, named but not
     defined on the pages): the same ranking as find_blocks, cut at a fixed
     count -- k blocks (K tokens / B), or the nearest integer to ratio * |valid|
@@ -40,7 +45,7 @@ from __future__ import annotations
 
 import math
 from dataclasses import dataclass
-from typing import Iterable, List, Optional, Sequence
+from typing import Iterable, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -292,3 +297,61 @@ def dit_run_density(sparse_density: float, steps: int = 50, warmup: int = 5) -> 
     steps count as density 1."""
     n_dense = sum(1 for t in range(steps) if dit_step_is_dense(t, warmup))
     return (n_dense + (steps - n_dense) * sparse_density) / steps
+
+
+# ---------------------------------------------------------------------------
+# Minimum threshold prediction (papercache.org summary, section 2.3 "minimum
+# threshold prediction"; chapterpal.com Knowl 3): per-head thresholds chosen by
+# dynamic programming over threshold-reduction steps, each step multiplying a
+# head's threshold by 0.9.  The pages' performance P(h, m) is downstream model
+# accuracy; here it is a proxy, minus the sum over heads of the relative
+# squared error of the head's sparse output against its dense output.
+# ---------------------------------------------------------------------------
+def head_rel_sq_error(O_sparse: np.ndarray, O_dense: np.ndarray) -> float:
+    """sum (O_sparse - O_dense)^2 / sum O_dense^2 over one head's [L][d] output."""
+    a = np.asarray(O_sparse, dtype=np.float64)
+    b = np.asarray(O_dense, dtype=np.float64)
+    den = float((b * b).sum())
+    return float(((a - b) ** 2).sum()) / den if den > 0 else 0.0
+
+
+def tau_levels(tau0: float, levels: int) -> List[float]:
+    """Threshold after k reduction steps, k = 0 .. levels: tau0 * 0.9^k."""
+    t, out = float(tau0), []
+    for _ in range(levels + 1):
+        out.append(t)
+        t *= 0.9
+    return out
+
+
+def tau_dp(err: np.ndarray, steps: int) -> Tuple[List[int], float]:
+    """Distribute exactly `steps` reduction steps over the heads.
+
+    err[h][k]: proxy error of head h after k steps (k = 0 .. R).  D[h][m] is
+    the best performance (minus the summed error) of heads 0 .. h-1 having
+    taken m steps in total; head h either keeps its level-0 threshold or takes
+    k steps on top of the best state with m - k steps over the heads before it
+    -- with R = 1 exactly the printed recurrence D[h][m] = max(D[h-1][m],
+    P(h, m)).  Ties keep the smaller k for the later head.  Returns the levels
+    per head (traced back from D[H][steps]) and that best value."""
+    err = np.asarray(err, dtype=np.float64)
+    H, R1 = err.shape
+    R = R1 - 1
+    assert 0 <= steps <= H * R, "steps must lie in [0, H*R]"
+    D = np.full((H + 1, steps + 1), -np.inf)
+    take = np.zeros((H + 1, steps + 1), dtype=np.int64)
+    D[0, 0] = 0.0
+    for h in range(1, H + 1):
+        for m in range(steps + 1):
+            for k in range(0, min(R, m) + 1):
+                if D[h - 1, m - k] == -np.inf:
+                    continue
+                cand = D[h - 1, m - k] - err[h - 1, k]
+                if cand > D[h, m]:
+                    D[h, m] = cand
+                    take[h, m] = k
+    levels, m = [0] * H, steps
+    for h in range(H, 0, -1):
+        levels[h - 1] = int(take[h, m])
+        m -= levels[h - 1]
+    return levels, float(D[H, steps])

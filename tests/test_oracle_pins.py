@@ -477,3 +477,63 @@ def test_dit_attention_sparse_step_is_restricted_attention():
         want = _naive_attention(Q, K, V, causal=False, allowed=allowed)[qb * B:(qb + 1) * B]
         np.testing.assert_allclose(O.dit_attention(Q, K, V, S, B, 0.6, 5, 5, qb), want,
                                    rtol=0, atol=1e-12)
+
+
+# --- minimum threshold prediction (per-head tau DP) ---------------------------
+def _monotone_errors(rng, H, R):
+    inc = rng.exponential(1.0, size=(H, R + 1))
+    inc[:, 0] = rng.uniform(0, 0.1, size=H)
+    return np.cumsum(inc, axis=1)
+
+
+@pytest.mark.parametrize("trial", range(25))
+def test_tau_dp_is_optimal_by_enumeration(trial):
+    rng = np.random.default_rng(4000 + trial)
+    H, R = int(rng.integers(1, 6)), int(rng.integers(1, 4))
+    err = _monotone_errors(rng, H, R)
+    if trial % 5 == 0:
+        err = np.round(err * 2) / 2          # exact ties
+    for steps in range(H * R + 1):
+        levels, best = O.tau_dp(err, steps)
+        assert sum(levels) == steps and all(0 <= k <= R for k in levels)
+        assert math.isclose(-sum(err[h, k] for h, k in enumerate(levels)), best,
+                            rel_tol=0, abs_tol=1e-12)
+        brute = max(-sum(err[h, k] for h, k in enumerate(ks))
+                    for ks in itertools.product(range(R + 1), repeat=H) if sum(ks) == steps)
+        assert math.isclose(best, brute, rel_tol=0, abs_tol=1e-12)
+
+
+def test_tau_dp_one_step_per_head_takes_the_cheapest_heads():
+    """R = 1 (the printed recurrence): the m reduced heads are those whose
+    error grows least from one step."""
+    rng = np.random.default_rng(44)
+    H = 12
+    err = _monotone_errors(rng, H, 1)
+    inc = err[:, 1] - err[:, 0]
+    for m in range(H + 1):
+        levels, _ = O.tau_dp(err, m)
+        assert sorted(h for h in range(H) if levels[h]) == sorted(np.argsort(inc)[:m].tolist())
+
+
+def test_tau_dp_extremes_and_levels():
+    err = _monotone_errors(np.random.default_rng(3), 6, 3)
+    assert O.tau_dp(err, 0)[0] == [0] * 6
+    assert O.tau_dp(err, 18)[0] == [3] * 6
+    t = O.tau_levels(0.9, 3)
+    np.testing.assert_allclose(t, [0.9, 0.81, 0.729, 0.6561], rtol=0, atol=1e-15)
+    # with one step per head (R = 1, steps = H) every head takes it: the mean
+    # threshold goes from 0.9 to 0.81 (the pages: from 0.9 to about 0.8)
+    lv, _ = O.tau_dp(err[:, :2], 6)
+    assert lv == [1] * 6
+    assert math.isclose(float(np.mean([O.tau_levels(0.9, 1)[k] for k in lv])), 0.81)
+
+
+def test_head_rel_sq_error_properties():
+    rng = np.random.default_rng(8)
+    b = rng.standard_normal((64, 16))
+    a = b + 0.01 * rng.standard_normal((64, 16))
+    assert O.head_rel_sq_error(b, b) == 0.0
+    assert O.head_rel_sq_error(np.zeros_like(b), b) == 1.0
+    assert math.isclose(O.head_rel_sq_error(3 * a, 3 * b), O.head_rel_sq_error(a, b), rel_tol=1e-12)
+    manual = sum(((a - b) ** 2).flat) / sum((b ** 2).flat)
+    assert math.isclose(O.head_rel_sq_error(a, b), manual, rel_tol=1e-12)
