@@ -322,6 +322,40 @@ def main():
             next_rows["f2_score_select_fused"] = {
                 "ms": round(ms_f, 3), "two_calls_ms": round(score_ms + select_ms, 3),
                 "density": round(int(counts.to(torch.int64).sum()) / valid, 5)}
+        # per-head threshold calibration: tau0 * 0.9^k (k = 0 .. 2) for every head,
+        # errors of the sparse outputs against the dense one, DP over hq steps
+        if cfg.dtype == "bf16":
+            R_lv, t0c = 2, float(np.max(w.tau))
+            dense = torch.empty_like(Q)
+            spo = torch.empty_like(Q)
+            torch.cuda.synchronize()
+            tc0 = time.perf_counter()
+            xattn.xattn_full(Q, K, V, cfg.causal, out=dense, stream=stream)
+            xattn.xattn_score(Q, K, cfg.S, cfg.B, cfg.causal, scores=scores, workspace=ws,
+                              stream=stream)
+            errs = []
+            for t in [t0c * 0.9 ** k for k in range(R_lv + 1)]:
+                xattn.xattn_select(scores, [t] * hq, cfg.causal, mask=mask, idx=idx,
+                                   counts=counts, stream=stream)
+                xattn.xattn_sparse_prefill(Q, K, V, cfg.B, idx, counts, cfg.causal, out=spo,
+                                           stream=stream)
+                errs.append(xattn.xattn_head_error(spo, dense, stream=stream).cpu().numpy())
+            err = np.stack(errs, axis=1)
+            levels, best = xattn.xattn_tau_dp(err, hq)
+            torch.cuda.synchronize()
+            calib_ms = (time.perf_counter() - tc0) * 1e3
+            tau_h = [t0c * 0.9 ** k for k in levels]
+            xattn.xattn_select(scores, tau_h, cfg.causal, mask=mask, idx=idx, counts=counts,
+                               stream=stream)
+            torch.cuda.synchronize()
+            d_cal = int(counts.to(torch.int64).sum()) / valid
+            next_rows["f4_tau_dp"] = {
+                "tau0": t0c, "levels": R_lv, "steps": hq, "calibration_ms": round(calib_ms, 1),
+                "mean_tau": round(float(np.mean(tau_h)), 4),
+                "heads_per_level": [levels.count(k) for k in range(R_lv + 1)],
+                "proxy_error_sum": round(-best, 6),
+                "density_calibrated": round(d_cal, 5), "density_uniform_tau0": round(n_sel / valid, 5)}
+            del dense, spo
         # video-DiT warm-up policy on the config-5 workload (non-causal video tokens)
         if args.next_dit:
             next_rows["f2_dit_policy"] = dit_policy_rows(timed, stream)

@@ -53,6 +53,16 @@ hipError_t launch_select_topk(int hq, int NB, int causal, const float* scores, i
 hipError_t launch_select_topratio(int hq, int NB, int causal, const float* scores, float ratio,
                                   uint64_t* mask, int32_t* idx, int32_t* counts, hipStream_t st);
 
+// ---- threshold calibration -----------------------------------------------------
+// err[h] = sum (O_sparse - O_dense)^2 / sum O_dense^2 over head h's per_head
+// elements (bf16 or fp32), accumulated in float64 in a fixed order.
+hipError_t launch_head_error(int hq, size_t per_head, bool bf16, const void* O_sparse,
+                             const void* O_dense, double* err, hipStream_t st);
+// Host DP: distributes exactly `steps` reduction steps over H heads with
+// err[h*(R+1) + k] the error of head h after k steps; writes levels[H] and
+// returns minus the summed error of the chosen levels.
+double tau_dp(int H, int R, const double* err, int steps, int* levels);
+
 // ---- attention ---------------------------------------------------------------
 // idx == nullptr selects dense mode (every key block, causal-limited).
 hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const void* V,

@@ -357,6 +357,39 @@ xattn_status xattn_dit_attention(const xattn_shape* shape, const void* Q, const 
   return hip_status(e, "xattn_dit_attention attention launch");
 }
 
+// ---- per-head threshold calibration -------------------------------------------
+
+xattn_status xattn_head_error(const xattn_shape* shape, const void* O_sparse, const void* O_dense,
+                              double* err, void* stream) {
+  xattn::Shape s;
+  xattn_status st = check_shape(shape, &s);
+  if (st != XATTN_OK) return st;
+  if (!O_sparse || !O_dense || !err)
+    return fail(XATTN_EINVAL, "O_sparse, O_dense and err must be non-NULL");
+  const size_t per_head = (size_t)s.L * s.d, esz = s.bf16 ? 2 : 4;
+  if ((per_head * esz) % 16 || ((uintptr_t)O_sparse | (uintptr_t)O_dense) % 16)
+    return fail(XATTN_EINVAL, "outputs must be 16-byte aligned with L*d*size a multiple of 16");
+  hipError_t e = xattn::launch_head_error(s.hq, per_head, s.bf16, O_sparse, O_dense, err,
+                                          (hipStream_t)stream);
+  return hip_status(e, "xattn_head_error launch");
+}
+
+xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, int32_t steps,
+                          int32_t* level_out, double* best_out) {
+  if (hq < 1 || levels < 0) return fail(XATTN_EINVAL, "hq (%d) >= 1 and levels (%d) >= 0 required", hq, levels);
+  if (!err_host || !level_out) return fail(XATTN_EINVAL, "err_host and level_out must be non-NULL");
+  if (steps < 0 || (int64_t)steps > (int64_t)hq * levels)
+    return fail(XATTN_EINVAL, "steps = %d is outside [0, hq * levels] = [0, %lld]", steps,
+                (long long)hq * levels);
+  if ((int64_t)(hq + 1) * (steps + 1) > (int64_t)1 << 26)
+    return fail(XATTN_EUNSUPPORTED, "DP table of %d x %d entries is too large", hq + 1, steps + 1);
+  for (int64_t i = 0; i < (int64_t)hq * (levels + 1); ++i)
+    if (!std::isfinite(err_host[i])) return fail(XATTN_EINVAL, "err_host[%lld] is not finite", (long long)i);
+  const double best = xattn::tau_dp(hq, levels, err_host, steps, level_out);
+  if (best_out) *best_out = best;
+  return ok();
+}
+
 const char* xattn_status_str(xattn_status status) {
   switch (status) {
     case XATTN_OK: return "ok";

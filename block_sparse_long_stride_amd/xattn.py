@@ -20,7 +20,8 @@ XATTN_FP32, XATTN_BF16 = 0, 1
 EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_score_pattern", "xattn_select",
            "xattn_select_topk",
            "xattn_select_topratio", "xattn_score_select", "xattn_sparse_prefill", "xattn_full",
-           "xattn_dit_workspace_bytes", "xattn_dit_attention", "xattn_status_str",
+           "xattn_dit_workspace_bytes", "xattn_dit_attention", "xattn_head_error", "xattn_tau_dp",
+           "xattn_status_str",
            "xattn_last_error", "xattn_version")
 
 
@@ -66,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.xattn_dit_workspace_bytes.restype = SZ
     L.xattn_dit_attention.argtypes = [SP, P, P, P, I32, I32, P, I32, I32, P, P, SZ, P]
     L.xattn_dit_attention.restype = I32
+    L.xattn_head_error.argtypes = [SP, P, P, P, P]
+    L.xattn_head_error.restype = I32
+    L.xattn_tau_dp.argtypes = [I32, I32, P, I32, P, P]
+    L.xattn_tau_dp.restype = I32
     L.xattn_sparse_prefill.argtypes = [SP, P, P, P, I32, P, P, P, P]
     L.xattn_sparse_prefill.restype = I32
     L.xattn_full.argtypes = [SP, P, P, P, P, P]
@@ -263,6 +268,38 @@ def xattn_dit_attention(Q, K, V, S: int, B: int, tau: Sequence[float], step: int
                                      int(warmup_steps), _ptr(out), _ptr(workspace), ws_bytes,
                                      _stream(stream)), "xattn_dit_attention")
     return out
+
+
+def xattn_head_error(O_sparse, O_dense, err=None, stream=None):
+    """Per-head relative squared error of two [hq][L][d] outputs (float64 [hq])."""
+    torch = _torch()
+    if O_sparse.shape != O_dense.shape or O_sparse.dtype != O_dense.dtype or O_sparse.dim() != 3:
+        raise ValueError("O_sparse and O_dense must be [hq][L][d] tensors of one dtype")
+    if not (O_sparse.is_contiguous() and O_dense.is_contiguous()):
+        raise ValueError("outputs must be contiguous")
+    hq, L, d = O_dense.shape
+    dt = XATTN_BF16 if O_dense.dtype == torch.bfloat16 else XATTN_FP32
+    sh = Shape(hq, hq, L, d, dt, 0)
+    if err is None:
+        err = torch.empty(hq, dtype=torch.float64, device=O_dense.device)
+    _check(lib().xattn_head_error(ctypes.byref(sh), _ptr(O_sparse), _ptr(O_dense), _ptr(err),
+                                  _stream(stream)), "xattn_head_error")
+    return err
+
+
+def xattn_tau_dp(err, steps: int) -> Tuple[list, float]:
+    """Host DP over threshold-reduction steps: err[h][k] (k = 0 .. levels)."""
+    import numpy as np
+    e = np.ascontiguousarray(np.asarray(err, dtype=np.float64))
+    if e.ndim != 2:
+        raise ValueError("err must be [hq][levels + 1]")
+    hq, r1 = e.shape
+    out = np.zeros(hq, dtype=np.int32)
+    best = ctypes.c_double(0.0)
+    _check(lib().xattn_tau_dp(hq, r1 - 1, e.ctypes.data_as(ctypes.c_void_p), int(steps),
+                              out.ctypes.data_as(ctypes.c_void_p), ctypes.byref(best)),
+           "xattn_tau_dp")
+    return [int(x) for x in out], float(best.value)
 
 
 def xattn_sparse_prefill(Q, K, V, B: int, idx, counts, causal: bool, out=None, stream=None):

@@ -17,6 +17,7 @@
  *   xattn_score_select   scoring + threshold selection fused (no score matrix)
  *   xattn_sparse_prefill attention over the selected blocks
  *   xattn_dit_attention  dense warm-up steps, then the sparse path (video DiT)
+ *   xattn_head_error, xattn_tau_dp  per-head threshold calibration
  *   xattn_full           dense attention (the speed baseline)
  *
  * Conventions for every call:
@@ -186,6 +187,33 @@ xattn_status xattn_dit_attention(const xattn_shape* shape, const void* Q, const 
                                  const void* V, int32_t S, int32_t B, const float* tau_host,
                                  int32_t step, int32_t warmup_steps, void* O, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * Minimum threshold prediction (section 2.3; chapterpal.com Knowl 3): per-head
+ * thresholds by dynamic programming over threshold-reduction steps, each step
+ * multiplying a head's threshold by 0.9.  The pages score a configuration by
+ * downstream model accuracy; these calls use a proxy computed on the device,
+ * the relative squared error of a head's sparse output against its dense
+ * output, and a host DP that is exact for that additive proxy.
+ *
+ * xattn_head_error: err[h] = sum (O_sparse - O_dense)^2 / sum O_dense^2 over
+ *   head h's [L][d] output (0 if O_dense is 0), float64, deterministic.
+ *   shape gives hq, L, d and dtype (hkv and causal are not used); O_sparse,
+ *   O_dense: device [hq][L][d], 16-byte aligned; err: device, hq doubles.
+ *
+ * xattn_tau_dp (host only, no device work): err_host[h*(levels+1) + k] is head
+ *   h's error after k steps (threshold tau0 * 0.9^k), k = 0 .. levels.
+ *   Exactly `steps` steps (0 .. hq*levels, else XATTN_EINVAL) are distributed
+ *   to maximise minus the summed error; D[h][m] is the best value over heads
+ *   0 .. h-1 with m steps (levels = 1 is the printed recurrence
+ *   D[h][m] = max(D[h-1][m], P(h, m))); ties keep the smaller level for the
+ *   later head.  Writes level_out[hq] (host) and, if non-NULL, *best_out.
+ *   Tables beyond 2^26 entries: XATTN_EUNSUPPORTED.
+ */
+xattn_status xattn_head_error(const xattn_shape* shape, const void* O_sparse, const void* O_dense,
+                              double* err, void* stream);
+xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, int32_t steps,
+                          int32_t* level_out, double* best_out);
 
 /*
  * Block-sparse attention (section 1, step 3): for query block qb of head h,

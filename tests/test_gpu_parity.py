@@ -346,3 +346,51 @@ def test_dit_attention_policy(name):
                                                        idx_np[h, qb, :cnt_np[h, qb]])
     assert_outputs_close(got_w, want_w, cfg.dtype)
     assert_outputs_close(got_s, want_s, cfg.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_head_error_matches_oracle(dtype):
+    """Per-head relative squared error on the device against the oracle's."""
+    import torch
+    from block_sparse_long_stride_amd import xattn_head_error
+    rng = np.random.default_rng(12)
+    hq, L, d = 5, 1536, 64
+    b = rng.standard_normal((hq, L, d))
+    a = b + rng.standard_normal((hq, L, d)) * np.array([0, 1e-3, 1e-2, 0.3, 1.0])[:, None, None]
+    b[4] = 0.0                                        # zero reference: error 0 by definition
+    tt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    A, Bt = torch.from_numpy(a).to(tt).cuda(), torch.from_numpy(b).to(tt).cuda()
+    got = xattn_head_error(A, Bt).cpu().numpy()
+    a_r, b_r = A.float().cpu().numpy(), Bt.float().cpu().numpy()   # the values the device sees
+    want = np.array([O.head_rel_sq_error(a_r[h], b_r[h]) for h in range(hq)])
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+    assert got[0] == 0.0 and got[4] == 0.0
+
+
+@pytest.mark.parametrize("name", ["llm-S8-B128", "video-ragged"])
+def test_tau_calibration_end_to_end(name):
+    """Calibration on the device: dense output once, then per level k the
+    threshold tau0 * 0.9^k for every head -> selection -> sparse prefill ->
+    head errors; the library DP on those errors equals the oracle DP and the
+    errors equal the oracle's on the same outputs."""
+    import torch
+    from block_sparse_long_stride_amd import (xattn_full, xattn_head_error, xattn_select,
+                                              xattn_sparse_prefill, xattn_tau_dp)
+    cfg, w, dev, ora = case(name)
+    R, tau0 = 2, 0.95
+    dense = xattn_full(dev["Q"], dev["K"], dev["V"], cfg.causal)
+    sc = _gpu_scores(cfg, dev)
+    errs, outs = [], []
+    for t in O.tau_levels(tau0, R):
+        _, idx, counts = xattn_select(sc, np.full(cfg.hq, t, np.float32), cfg.causal)
+        o = xattn_sparse_prefill(dev["Q"], dev["K"], dev["V"], cfg.B, idx, counts, cfg.causal)
+        errs.append(xattn_head_error(o, dense).cpu().numpy())
+        outs.append(o.float().cpu().numpy())
+    _sync()
+    err = np.stack(errs, axis=1)                      # [hq][R+1]
+    d32 = dense.float().cpu().numpy()
+    want = np.array([[O.head_rel_sq_error(outs[k][h], d32[h]) for k in range(R + 1)]
+                     for h in range(cfg.hq)])
+    np.testing.assert_allclose(err, want, rtol=1e-12, atol=0)
+    for steps in range(cfg.hq * R + 1):
+        assert xattn_tau_dp(err, steps) == O.tau_dp(err, steps)
