@@ -23,6 +23,8 @@
 // Kernel 2 (score_fixup): per 32 reshaped rows, combines the range snapshots
 // into the row's softmax max and denominator, rescales the partial block sums,
 // adds the B/S rows of each query block and divides by B/S.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 #include "select_row.h"
@@ -49,7 +51,8 @@ struct GemmParams {
   float* M;   // [hq][nR32][nct][32]
   float* Z;   // [hq][nR32][nct][32]
   int L, S, group, NB, Lr, nR32, nct;
-  int causal, ntr, ntc, tiles_per_head, nwork, grid;
+  int causal, ntr, ntc, tiles_per_head, nwork;
+  int per_xcd, wg_per_xcd;   // work items per XCD, workgroups per XCD
   float scale_log2;
   PhaseMap phase;   // key sub-row per query sub-row (default: antidiagonal)
 };
@@ -61,156 +64,96 @@ __device__ __forceinline__ int chunk_off(int row, int piece) {
   return row * 64 + ((piece ^ ((row >> 2) & 3)) << 4);
 }
 
-__device__ __forceinline__ void wait_vmem_dma() {
-  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");   // kDmaPerWave copies may stay in flight
+// Copies of the two chunks after next may stay in flight (three chunks are
+// ahead when the next one is needed).
+__device__ __forceinline__ void wait_next_chunk() {
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
-template <int D, int BS>
-__global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
-  static_assert(kDmaPerWave == 4, "wait_vmem_dma assumes four copies per wave per chunk");
-  // Three LDS stages as distinct objects (the chunk loop is unrolled by three)
-  // so LDS reads of one stage never wait on the direct-to-LDS copies into another.
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
-
-  const int w = xcd_swizzle(blockIdx.x, p.grid);
-  if (w >= p.nwork) return;
-  // work order: (kv group, tile, query head within group), heads fastest
-  const int hh = w % p.group;
-  const int t = (w / p.group) % p.tiles_per_head;
-  const int g = w / (p.group * p.tiles_per_head);
-  const int h = g * p.group + hh;
-  int tr, tc;
-  if (p.causal) {   // square tiles: row tr holds column tiles 0 .. tr
-    tr = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
-    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
-    while (tr * (tr + 1) / 2 > t) --tr;
-    tc = t - tr * (tr + 1) / 2;
-  } else {
-    tr = t / p.ntc;
-    tc = t % p.ntc;
-  }
-  const int R0 = tr * kTileR, C0 = tc * kTileC;
-  const int F = p.S * D;
-  const int Lr = p.Lr;
-  const uint16_t* Qh = p.Q + (size_t)h * p.L * D;
-  const uint16_t* Kg = p.K + (size_t)g * p.L * D;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wc = wave % kWavesC, wr = wave / kWavesC;
-  const int l32 = lane & 31, hi = lane >> 5;
-
-  // Direct-to-LDS copies through buffer resources (buffer_load ... lds).  A
-  // stage holds kTileC key rows then kTileR query rows; copy n (1 KB) fills
-  // rows 16n .. 16n+15, lane -> row 16n + lane/4 and piece lane % 4.  Each
-  // lane's byte offset is fixed for the whole K loop (no address register is
-  // rewritten while copies are in flight); the chunk only moves the scalar
-  // offset.  Rows past Lr (ragged last tile) re-read row Lr-1: finite data
-  // whose products are masked or never stored.
-  const __amdgpu_buffer_rsrc_t rsrc_k =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Kg, (short)0, p.L * D * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rsrc_q =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, p.L * D * 2, 0x00020000);
-  uint32_t dma_off[kDmaPerWave];
+// Epilogue of a wave with no masked column: per row R (one per lane and
+// 32-row block j) the range max (the scale is positive, so the max of the
+// scaled values is the scaled max), the range sum of exp2(z - m) and the
+// per-key-block sums.  Each block sum is finished by one exchange between
+// the two half-waves: a lane keeps the four-column sums of the block it
+// stores and hands the other half-wave's block to its partner, so every lane
+// stores and no store is predicated beyond the row bound.
+template <int BS>
+__device__ __forceinline__ void epilogue_interior(const GemmParams& p, f32x16_t (&acc)[2][4], int h,
+                                                  int R_lane0, int cw, int ct, int hi) {
+  const int kb0 = cw / BS;
 #pragma unroll
-  for (int k = 0; k < kDmaPerWave; ++k) {
-    const int n = k * kWaves + wave;
-    const int row = n * 16 + (lane >> 2);
-    const int piece = (lane & 3) ^ ((row >> 2) & 3);
-    if (k < kDmaK) {   // copies 0 .. kDmaK-1 of every wave cover the key rows
-      const int C = min(C0 + row, Lr - 1);
-      dma_off[k] = (uint32_t)(C * p.S * D * 2 + piece * 16);
-    } else {
-      const int R = min(R0 + row - kTileC, Lr - 1);
-      dma_off[k] = (uint32_t)(R * F * 2 + piece * 16);
+  for (int j = 0; j < 4; ++j) {
+    const int R = R_lane0 + j * 32;
+    float mr = acc[0][j][0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mr = fmaxf(mr, acc[i][j][v]);
+    float m = mr * p.scale_log2;
+    m = fmaxf(m, __shfl_xor(m, 32));
+    float s[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float acc4 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc4 += fast_exp2(acc[i][j][4 * q + r] * p.scale_log2 - m);
+        s[i][q] = acc4;
+      }
+    float zsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) zsum += s[i][q];
+    zsum += __shfl_xor(zsum, 32);
+    if (R >= p.Lr) continue;
+    const size_t rowbase = (size_t)h * p.nR32 + (R >> 5);
+    if (hi == 0) {
+      p.M[(rowbase * p.nct + ct) * 32 + (R & 31)] = m;
+      p.Z[(rowbase * p.nct + ct) * 32 + (R & 31)] = zsum;
     }
-  }
-  const int nk = F / kKC;
-  auto issue = [&](int kc, uint8_t* stage) __attribute__((always_inline)) {
-    kc = min(kc, nk - 1);   // past the end: harmless reload, keeps the copy count fixed
-    const int f0 = kc * kKC;
-    const int a = f0 / D, e0 = f0 % D;
-    // key operand: sub-row S-1-a of key group c (the stride reshape, reversed
-    // phase), or the sub-row the sampling pattern pairs with query sub-row a
-    const int ka = p.phase.custom ? p.phase.v[a] : p.S - 1 - a;
-    const uint32_t koff = (uint32_t)((ka * D + e0) * 2);
-    const uint32_t qoff = (uint32_t)(f0 * 2);
-#pragma unroll
-    for (int k = 0; k < kDmaPerWave; ++k) {
-      const int n = k * kWaves + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < kDmaK ? rsrc_k : rsrc_q,
-                                               (__attribute__((address_space(3))) void*)(stage + n * 1024),
-                                               16, dma_off[k], k < kDmaK ? koff : qoff, 0, 0);
-    }
-  };
-
-  // a wave whose whole column range lies right of its last row is fully masked
-  const bool wave_live = !p.causal || (C0 + wc * kWaveCols <= R0 + wr * kWaveRows + kWaveRows - 1);
-
-  // fragment offsets: A = key rows 64wc + 32i + l32, B = query rows
-  // 128wr + 32j + l32; both swizzles depend on l32 only
-  int aoff[2], boff[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    aoff[ks] = chunk_off(wc * 64 + l32, 2 * ks + hi);
-    boff[ks] = kTileC * 64 + chunk_off(wr * kWaveRows + l32, 2 * ks + hi);
-  }
-
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
-
-  auto compute = [&](const uint8_t* stage) __attribute__((always_inline)) {
-    // all fragments of the chunk are read before the first MFMA, so one LDS
-    // latency is exposed per chunk instead of one per k-step
-    bf16x8_t af[2][2], bfr[2][4];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[ks][i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[ks][j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    float* Prow = p.P + rowbase * p.NB * 32 + (R & 31);
+    if constexpr (BS == 4) {   // lane half hi holds blocks kb0 + 8i + 2q + hi
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // 12 DS reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
-  };
-  // One chunk: copy chunk kc+2 into the stage freed last chunk, multiply chunk
-  // kc, wait until chunk kc+1 has landed, synchronise.
-  auto step = [&](int kc, const uint8_t* cur, uint8_t* nxt) __attribute__((always_inline)) {
-    issue(kc + 2, nxt);
-    if (kc < nk && wave_live) compute(cur);
-    wait_vmem_dma();
-    __builtin_amdgcn_s_barrier();
-  };
-  issue(0, st0);
-  issue(1, st1);
-  wait_vmem_dma();
-  __builtin_amdgcn_s_barrier();
-  for (int kc = 0; kc < nk; kc += 3) {
-    step(kc, st0, st2);
-    step(kc + 1, st1, st0);
-    step(kc + 2, st2, st1);
+        for (int q = 0; q < 4; ++q) Prow[(size_t)(kb0 + 8 * i + 2 * q + hi) * 32] = s[i][q];
+    } else if constexpr (BS == 8) {   // block kb0 + 4i + q: sums s[i][q] of both halves
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const float keep = hi ? s[i][2 * qq + 1] : s[i][2 * qq];
+          const float give = hi ? s[i][2 * qq] : s[i][2 * qq + 1];
+          Prow[(size_t)(kb0 + 4 * i + 2 * qq + hi) * 32] = keep + __shfl_xor(give, 32);
+        }
+    } else if constexpr (BS == 16) {   // block kb0 + 2i + b: pairs (2b, 2b+1) of both halves
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float t0 = s[i][0] + s[i][1], t1 = s[i][2] + s[i][3];
+        const float keep = hi ? t1 : t0, give = hi ? t0 : t1;
+        Prow[(size_t)(kb0 + 2 * i + hi) * 32] = keep + __shfl_xor(give, 32);
+      }
+    } else {   // BS == 32: block kb0 + i, all four sums of both halves
+      float t[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) t[i] = s[i][0] + s[i][1] + s[i][2] + s[i][3];
+      const float keep = hi ? t[1] : t[0], give = hi ? t[0] : t[1];
+      Prow[(size_t)(kb0 + hi) * 32] = keep + __shfl_xor(give, 32);
+    }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (!wave_live) return;
+}
 
-  // ---- epilogue: per reshaped row R (one per lane and R-tile) ---------------
-  const int cw = C0 + wc * kWaveCols;   // first column of this wave's range
-  const int ct = cw / kWaveCols;
+// Epilogue of a diagonal or ragged wave: columns c > R (causal) or c >= Lr
+// are masked to -inf before the range max and sums.
+template <int BS>
+__device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&acc)[2][4], int h,
+                                                int R_lane0, int cw, int ct, int hi) {
+  const int Lr = p.Lr;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int R = R0 + wr * kWaveRows + j * 32 + l32;
+    const int R = R_lane0 + j * 32;
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -290,6 +233,215 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
       }
     }
   }
+}
+
+// Tile of work item w: work order (kv group, tile, query head within group),
+// heads fastest; causal tiles are the lower triangle, row tr holding column
+// tiles 0 .. tr.
+struct TileItem {
+  int h, g, R0, C0;
+};
+
+__device__ __forceinline__ TileItem decode_item(const GemmParams& p, int w) {
+  const int hh = w % p.group;
+  const int t = (w / p.group) % p.tiles_per_head;
+  const int g = w / (p.group * p.tiles_per_head);
+  int tr, tc;
+  if (p.causal) {
+    tr = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((tr + 1) * (tr + 2) / 2 <= t) ++tr;
+    while (tr * (tr + 1) / 2 > t) --tr;
+    tc = t - tr * (tr + 1) / 2;
+  } else {
+    tr = t / p.ntc;
+    tc = t % p.ntc;
+  }
+  return TileItem{g * p.group + hh, g, tr * kTileR, tc * kTileC};
+}
+
+// Persistent scoring GEMM.  Workgroups are dealt round-robin to the XCDs, so
+// workgroup b runs on XCD b % 8; XCD x owns the work items
+// [x * per_xcd, (x + 1) * per_xcd) and its wg_per_xcd workgroups (one per
+// CU) take every wg_per_xcd-th of them, so at any time one XCD's CUs work on
+// consecutive items -- a few column tiles of one tile row for all query
+// heads of one KV group -- and share their Q and K rows through its L2.
+// The copy pipeline runs across items: the last three chunk steps of an
+// item already copy the next item's first three chunks, which land while
+// the item's epilogue runs.
+template <int D, int BS, bool PATTERN>
+__global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
+  static_assert(kDmaPerWave == 4, "wait_next_chunk assumes four copies per wave per chunk");
+  // Four LDS stages as distinct objects (the chunk loop is unrolled by four)
+  // so LDS reads of one stage never wait on the direct-to-LDS copies into another.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
+
+  const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
+  const int first = xcd * p.per_xcd + slot;
+  const int end = min(xcd * p.per_xcd + p.per_xcd, p.nwork);
+  if (first >= end) return;
+  const int nitems = (end - first + p.wg_per_xcd - 1) / p.wg_per_xcd;
+
+  const int F = p.S * D;
+  const int Lr = p.Lr;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wc = wave % kWavesC, wr = wave / kWavesC;
+  const int l32 = lane & 31, hi = lane >> 5;
+  // a sampling pattern's key sub-row for query sub-row a, held in lane a
+  // (patterns cover S <= 64), read with one lane read instead of a scalar load
+  const int phase_lane = PATTERN ? p.phase.v[lane] : 0;
+
+  // Direct-to-LDS copies through buffer resources (buffer_load ... lds).  A
+  // stage holds kTileC key rows then kTileR query rows; copy n (1 KB) fills
+  // rows 16n .. 16n+15, lane -> row 16n + lane/4 and piece lane % 4.  Each
+  // lane's byte offset is fixed per item (no address register is rewritten
+  // while copies from it are in flight: the next item's offsets live in their
+  // own registers); the chunk only moves the scalar offset.  Rows past Lr
+  // (ragged last tile) re-read row Lr-1: finite data whose products are
+  // masked or never stored.
+  // Copy source of one item: its query head, KV group and the per-lane byte
+  // offsets of its rows (the chunk adds a scalar offset).
+  auto row_offsets = [&](const TileItem& t, uint32_t (&off)[kDmaPerWave]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+      const int n = k * kWaves + wave;
+      const int row = n * 16 + (lane >> 2);
+      const int piece = (lane & 3) ^ ((row >> 2) & 3);
+      if (k < kDmaK) {   // copies 0 .. kDmaK-1 of every wave cover the key rows
+        const int C = min(t.C0 + row, Lr - 1);
+        off[k] = (uint32_t)(C * p.S * D * 2 + piece * 16);
+      } else {
+        const int R = min(t.R0 + row - kTileC, Lr - 1);
+        off[k] = (uint32_t)(R * F * 2 + piece * 16);
+      }
+    }
+  };
+  const int nk = F / kKC;
+  const int nkp = (nk + 3) & ~3;   // chunk steps per item (steps past nk reload chunk nk-1)
+  auto issue = [&](int h_, int g_, const uint32_t (&off)[kDmaPerWave], int kc, uint8_t* stage)
+                   __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.K + (size_t)g_ * p.L * D), (short)0, p.L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.Q + (size_t)h_ * p.L * D), (short)0, p.L * D * 2, 0x00020000);
+    kc = min(kc, nk - 1);
+    const int f0 = kc * kKC;
+    const int a = f0 / D, e0 = f0 % D;
+    // key operand: sub-row S-1-a of key group c (the stride reshape, reversed
+    // phase), or the sub-row the sampling pattern pairs with query sub-row a
+    const int ka = PATTERN ? __builtin_amdgcn_readlane(phase_lane, a) : p.S - 1 - a;
+    const uint32_t koff = (uint32_t)((ka * D + e0) * 2);
+    const uint32_t qoff = (uint32_t)(f0 * 2);
+#pragma unroll
+    for (int k = 0; k < kDmaPerWave; ++k) {
+      const int n = k * kWaves + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k < kDmaK ? rk : rq,
+                                               (__attribute__((address_space(3))) void*)(stage + n * 1024),
+                                               16, off[k], k < kDmaK ? koff : qoff, 0, 0);
+    }
+  };
+
+  // fragment offsets: A = key rows 64wc + 32i + l32, B = query rows
+  // 128wr + 32j + l32; both swizzles depend on l32 only
+  int aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = chunk_off(wc * 64 + l32, 2 * ks + hi);
+    boff[ks] = kTileC * 64 + chunk_off(wr * kWaveRows + l32, 2 * ks + hi);
+  }
+
+  f32x16_t acc[2][4];
+  auto compute = [&](const uint8_t* stage) __attribute__((always_inline)) {
+    // all fragments of the chunk are read before the first MFMA, so one LDS
+    // latency is exposed per chunk instead of one per k-step
+    bf16x8_t af[2][2], bfr[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[ks][i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[ks][j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // 12 DS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
+  };
+
+  TileItem it = decode_item(p, first);
+  // the item after this one (or this one again after the last: harmless reloads)
+  TileItem nx = nitems > 1 ? decode_item(p, first + p.wg_per_xcd) : it;
+  uint32_t cur_off[kDmaPerWave], nxt_off[kDmaPerWave];
+  row_offsets(it, cur_off);
+  row_offsets(nx, nxt_off);
+  int cur_h = it.h, cur_g = it.g, nxt_h = nx.h, nxt_g = nx.g;
+  // One chunk step kc of the current item: copy step kc+3 into the stage read
+  // in step kc-1 (every wave is past the barrier that followed it), multiply
+  // chunk kc, wait until step kc+1 has landed, synchronise.  Step kc+3 is a
+  // chunk of this item, or in the item's last three steps one of the next
+  // item's first three chunks.
+  auto step = [&](int kc, bool live, bool to_next, const uint8_t* cur_st, uint8_t* refill)
+                  __attribute__((always_inline)) {
+    if (to_next) issue(nxt_h, nxt_g, nxt_off, kc + 3 - nkp, refill);
+    else issue(cur_h, cur_g, cur_off, kc + 3, refill);
+    if (live && kc < nk) compute(cur_st);
+    wait_next_chunk();
+    __builtin_amdgcn_s_barrier();
+  };
+  issue(cur_h, cur_g, cur_off, 0, st0);
+  issue(cur_h, cur_g, cur_off, 1, st1);
+  issue(cur_h, cur_g, cur_off, 2, st2);
+  wait_next_chunk();
+  __builtin_amdgcn_s_barrier();
+  for (int k = 0; k < nitems; ++k) {
+    // a wave whose whole column range lies right of its last row is fully masked
+    const bool live = !p.causal || (it.C0 + wc * kWaveCols <= it.R0 + wr * kWaveRows + kWaveRows - 1);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+    for (int kc = 0; kc < nkp - 4; kc += 4) {
+      step(kc, live, false, st0, st3);
+      step(kc + 1, live, false, st1, st0);
+      step(kc + 2, live, false, st2, st1);
+      step(kc + 3, live, false, st3, st2);
+    }
+    step(nkp - 4, live, false, st0, st3);
+    step(nkp - 3, live, true, st1, st0);
+    step(nkp - 2, live, true, st2, st1);
+    step(nkp - 1, live, true, st3, st2);
+    if (live) {
+      const int cw = it.C0 + wc * kWaveCols;   // first column of this wave's range
+      const int ct = cw / kWaveCols;
+      const int Rw = it.R0 + wr * kWaveRows;   // first row of this wave
+      // Interior waves (every column valid and, if causal, at or left of the
+      // wave's first row) need no mask.
+      if (cw + kWaveCols <= Lr && (!p.causal || cw + kWaveCols - 1 <= Rw))
+        epilogue_interior<BS>(p, acc, it.h, Rw + l32, cw, ct, hi);
+      else
+        epilogue_masked<BS>(p, acc, it.h, Rw + l32, cw, ct, hi);
+    }
+    it = nx;
+    cur_h = nxt_h;
+    cur_g = nxt_g;
+#pragma unroll
+    for (int q = 0; q < kDmaPerWave; ++q) cur_off[q] = nxt_off[q];
+    if (k + 2 < nitems) {
+      nx = decode_item(p, first + (k + 2) * p.wg_per_xcd);
+      row_offsets(nx, nxt_off);
+      nxt_h = nx.h;
+      nxt_g = nx.g;
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 struct FixupParams {
@@ -441,7 +593,9 @@ __global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams
 
 template <int D, int BS>
 hipError_t launch_gemm(const GemmParams& gp, hipStream_t st) {
-  hipLaunchKernelGGL((score_gemm<D, BS>), dim3(gp.grid), dim3(kWaves * 64), 0, st, gp);
+  const dim3 grid(gp.wg_per_xcd * kNumXcd), block(kWaves * 64);
+  if (gp.phase.custom) hipLaunchKernelGGL((score_gemm<D, BS, true>), grid, block, 0, st, gp);
+  else hipLaunchKernelGGL((score_gemm<D, BS, false>), grid, block, 0, st, gp);
   return hipGetLastError();
 }
 
@@ -454,6 +608,21 @@ hipError_t launch_gemm_bs(const GemmParams& gp, int bs, hipStream_t st) {
     case 32: return launch_gemm<D, 32>(gp, st);
   }
   return hipErrorInvalidValue;
+}
+
+// Compute units per XCD of the current device (the persistent GEMM runs one
+// workgroup per CU).
+int cus_per_xcd() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kNumXcd)
+      n = 256;
+    cached[dev] = n / kNumXcd;
+  }
+  return cached[dev];
 }
 
 struct WsLayout {
@@ -506,7 +675,8 @@ hipError_t run_score_gemm(const Shape& s, const void* Q, const void* K, int S, i
   gp.ntc = (wl.Lr + kTileC - 1) / kTileC;
   gp.tiles_per_head = s.causal ? gp.ntr * (gp.ntr + 1) / 2 : gp.ntr * gp.ntc;
   gp.nwork = gp.tiles_per_head * s.hq;
-  gp.grid = (gp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
+  gp.per_xcd = (gp.nwork + kNumXcd - 1) / kNumXcd;
+  gp.wg_per_xcd = std::min(gp.per_xcd, cus_per_xcd());
   gp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d * S));
   gp.phase = phase;
   const int bs = B / S;
