@@ -466,12 +466,15 @@ __device__ __forceinline__ void row_stats(const float* M, const float* Z, int r,
     nct_r = min(nct, last / kWaveCols + 1);
   }
   float m = -INFINITY;
-  if (R < Lr)
+  if (R < Lr) {
+#pragma unroll 4
     for (int c = sub; c < nct_r; c += 8) m = fmaxf(m, M[c * 32 + r]);
+  }
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   float z = 0.f;
   if (R < Lr && m != -INFINITY)
+#pragma unroll 4
     for (int c = sub; c < nct_r; c += 8) {
       const float mc = M[c * 32 + r];
       if (mc != -INFINITY) z += Z[c * 32 + r] * fast_exp2(mc - m);
@@ -483,22 +486,27 @@ __device__ __forceinline__ void row_stats(const float* M, const float* Z, int r,
 }
 
 // Block score of key block kb for the query block whose reshaped rows are
-// r0 .. r0+bs-1 of the group: the rows' partial block sums rescaled to the
-// rows' final softmax, summed in row order, divided by bs.
+// r0 .. r0+BS-1 of the group: the rows' partial block sums rescaled to the
+// rows' final softmax, summed in row order, divided by BS.  The BS row loads
+// are independent and issued together.
+template <int BS>
 __device__ __forceinline__ float block_score(const float* P, const float* M, const float* s_mfin,
-                                             const float* s_invz, int kb, int r0, int bs,
-                                             float inv_bs) {
-  const int c = (kb * bs) / kWaveCols;
+                                             const float* s_invz, int kb, int r0) {
+  const int c = (kb * BS) / kWaveCols;
   float acc = 0.f;
-  for (int r = r0; r < r0 + bs; ++r) {
+#pragma unroll
+  for (int u = 0; u < BS; ++u) {
+    const int r = r0 + u;
     const float mc = M[c * 32 + r];
-    if (mc == -INFINITY) continue;
-    acc += P[(size_t)kb * 32 + r] * fast_exp2(mc - s_mfin[r]) * s_invz[r];
+    const float pv = P[(size_t)kb * 32 + r];
+    if (mc != -INFINITY) acc += pv * fast_exp2(mc - s_mfin[r]) * s_invz[r];
   }
-  return acc * inv_bs;
+  return acc * (1.0f / (float)BS);
 }
 
-// One workgroup per (head, 32 reshaped rows).
+// One workgroup per (head, 32 reshaped rows); BS = B/S reshaped rows per
+// query block.
+template <int BS>
 __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   __shared__ float s_mfin[32];
   __shared__ float s_invz[32];
@@ -514,7 +522,7 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   {
     const int r = tid >> 3, sub = tid & 7;
     float m, invz;
-    row_stats(M, Z, r, rg * 32 + r, p.Lr, p.nct, p.bs, p.causal, sub, m, invz);
+    row_stats(M, Z, r, rg * 32 + r, p.Lr, p.nct, BS, p.causal, sub, m, invz);
     if (sub == 0) {
       s_mfin[r] = m;
       s_invz[r] = invz;
@@ -523,15 +531,14 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   __syncthreads();
 
   // 2. block scores for the 32/bs query blocks of this row group
-  const int nq = 32 / p.bs;
+  constexpr int nq = 32 / BS;
   const int qb0 = rg * nq;
-  const float inv_bs = 1.0f / (float)p.bs;
+#pragma unroll 2
   for (int it = tid; it < nq * p.NB; it += blockDim.x) {
     const int kb = it / nq, q = it % nq;
     const int qb = qb0 + q;
     if (qb >= p.NB) continue;
-    const float out = (!p.causal || kb <= qb)
-                          ? block_score(P, M, s_mfin, s_invz, kb, q * p.bs, p.bs, inv_bs) : 0.f;
+    const float out = (!p.causal || kb <= qb) ? block_score<BS>(P, M, s_mfin, s_invz, kb, q * BS) : 0.f;
     p.scores[((size_t)h * p.NB + qb) * p.NB + kb] = out;
   }
 }
@@ -552,7 +559,7 @@ struct FusedParams {
   TauArray tau;
 };
 
-template <int CAP>
+template <int CAP, int BS>
 __global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams p) {
   __shared__ SelectScratch<CAP> sh;
   __shared__ float s_row[CAP];
@@ -573,16 +580,15 @@ __global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams
     const bool used = rl < p.bs;
     const int r = r0 + (used ? rl : 0);
     float m, invz;
-    row_stats(M, Z, r, used ? rg * 32 + r : p.Lr, p.Lr, p.nct, p.bs, p.causal, sub, m, invz);
+    row_stats(M, Z, r, used ? rg * 32 + r : p.Lr, p.Lr, p.nct, BS, p.causal, sub, m, invz);
     if (used && sub == 0) {
       s_mfin[r] = m;
       s_invz[r] = invz;
     }
   }
   __syncthreads();
-  const float inv_bs = 1.0f / (float)p.bs;
   for (int kb = tid; kb < p.NB; kb += kSelectThreads)
-    s_row[kb] = (!p.causal || kb <= qb) ? block_score(P, M, s_mfin, s_invz, kb, r0, p.bs, inv_bs)
+    s_row[kb] = (!p.causal || kb <= qb) ? block_score<BS>(P, M, s_mfin, s_invz, kb, r0)
                                         : 0.f;
   __syncthreads();
   const CutSpec cut{kThreshold, 0, 0.f, p.tau.v[h]};
@@ -685,7 +691,14 @@ hipError_t run_score_gemm(const Shape& s, const void* Q, const void* K, int S, i
 
 template <int CAP>
 hipError_t launch_fused(const FusedParams& fp, int rows, hipStream_t st) {
-  hipLaunchKernelGGL((score_select_fused<CAP>), dim3(rows), dim3(kSelectThreads), 0, st, fp);
+  const dim3 grid(rows), block(kSelectThreads);
+  switch (fp.bs) {
+    case 4: hipLaunchKernelGGL((score_select_fused<CAP, 4>), grid, block, 0, st, fp); break;
+    case 8: hipLaunchKernelGGL((score_select_fused<CAP, 8>), grid, block, 0, st, fp); break;
+    case 16: hipLaunchKernelGGL((score_select_fused<CAP, 16>), grid, block, 0, st, fp); break;
+    case 32: hipLaunchKernelGGL((score_select_fused<CAP, 32>), grid, block, 0, st, fp); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -708,7 +721,14 @@ hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S
   fp.nct = wl.nct;
   fp.bs = B / S;
   fp.causal = s.causal;
-  hipLaunchKernelGGL(score_fixup, dim3(s.hq * wl.nR32), dim3(256), 0, st, fp);
+  const dim3 grid(s.hq * wl.nR32), block(256);
+  switch (fp.bs) {
+    case 4: hipLaunchKernelGGL(score_fixup<4>, grid, block, 0, st, fp); break;
+    case 8: hipLaunchKernelGGL(score_fixup<8>, grid, block, 0, st, fp); break;
+    case 16: hipLaunchKernelGGL(score_fixup<16>, grid, block, 0, st, fp); break;
+    case 32: hipLaunchKernelGGL(score_fixup<32>, grid, block, 0, st, fp); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
