@@ -14,7 +14,7 @@
 // chunk reads (a permutation of 0 .. S-1), so they run the same kernel.
 //
 // Kernel 1 (score_gemm): MFMA 32x32x16 bf16 GEMM over lower-triangular (causal)
-// or all 128x128 tiles of the reshaped matrix, computed transposed (rows =
+// or all 256x256 tiles of the reshaped matrix, computed transposed (rows =
 // key columns c, columns = query rows R) so that each lane owns one reshaped
 // row R.  Its epilogue masks c > R, scales by log2(e)/sqrt(d*S) and, per
 // 64-column range of each row, writes the range max m, the range sum of
@@ -34,15 +34,18 @@ namespace {
 
 constexpr int kWavesC = 4;       // waves along c
 constexpr int kWavesR = 2;       // waves along R
-constexpr int kWaves = kWavesC * kWavesR;
-constexpr int kTileC = 64 * kWavesC;    // reshaped columns c per workgroup tile
-constexpr int kTileR = 256;      // reshaped rows R per workgroup tile
-constexpr int kWaveCols = 64;    // columns per wave (and per softmax snapshot)
-constexpr int kWaveRows = 128;   // rows per wave
-constexpr int kKC = 32;          // reduction chunk (elements of S*d): 64-byte LDS rows
-constexpr int kStageBytes = (kTileC + kTileR) * kKC * 2;
-constexpr int kDmaPerWave = (kTileC + kTileR) * kKC * 2 / 1024 / kWaves;   // 1 KB copies per wave per chunk
-constexpr int kDmaK = kTileC * kKC * 2 / 1024 / kWaves;   // of which key-row copies
+constexpr int kWaves = kWavesC * kWavesR;   // two waves per SIMD
+constexpr int kWaveC = 64;       // key columns c per wave
+constexpr int kWaveR = 128;      // query rows R per wave
+constexpr int kTileC = kWaveC * kWavesC;    // reshaped columns c per workgroup tile
+constexpr int kTileR = kWaveR * kWavesR;    // reshaped rows R per workgroup tile
+constexpr int kRangeCols = 64;   // columns per softmax snapshot
+constexpr int kKC = 64;          // reduction chunk (elements of S*d): 128-byte LDS rows
+constexpr int kRowBytes = kKC * 2;
+constexpr int kStageBytes = (kTileC + kTileR) * kRowBytes;   // 64 KB
+constexpr int kRowsPerCopy = 1024 / kRowBytes;               // rows per 1 KB copy
+constexpr int kDmaPerWave = kStageBytes / 1024 / kWaves;     // 1 KB copies per wave per chunk
+constexpr int kDmaK = kTileC * kRowBytes / 1024 / kWaves;    // of which key-row copies
 
 struct GemmParams {
   const uint16_t* Q;
@@ -57,38 +60,32 @@ struct GemmParams {
   PhaseMap phase;   // key sub-row per query sub-row (default: antidiagonal)
 };
 
-// LDS rows hold one 32-element (64-byte) chunk of a reshaped row; their four
-// 16-byte pieces are XOR-swizzled by (row / 4) mod 4 so that 16 consecutive
-// rows read at the same piece fall in distinct bank groups (64 banks).
-__device__ __forceinline__ int chunk_off(int row, int piece) {
-  return row * 64 + ((piece ^ ((row >> 2) & 3)) << 4);
-}
+// LDS rows hold one 64-element (128-byte) chunk of a reshaped row; their
+// eight 16-byte pieces are XOR-swizzled by (row / 2) mod 8, so that 16
+// consecutive rows read at the same piece fall in 16 distinct 16-byte bank
+// groups (64 four-byte banks): conflict-free 16-byte fragment reads.
+__device__ __forceinline__ int piece_slot(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
-// Copies of the two chunks after next may stay in flight (three chunks are
-// ahead when the next one is needed).
-__device__ __forceinline__ void wait_next_chunk() {
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-}
-
-// Epilogue of a wave with no masked column: per row R (one per lane and
-// 32-row block j) the range max (the scale is positive, so the max of the
-// scaled values is the scaled max), the range sum of exp2(z - m) and the
-// per-key-block sums.  Each block sum is finished by one exchange between
-// the two half-waves: a lane keeps the four-column sums of the block it
-// stores and hands the other half-wave's block to its partner, so every lane
-// stores and no store is predicated beyond the row bound.
-template <int BS>
+// Epilogue of a wave's 64-column range (accumulator blocks I0, I0+1) with no
+// masked column: per row R (one per lane and 32-row block j) the range max
+// (the scale is positive, so the max of the scaled values is the scaled
+// max), the range sum of exp2(z - m) and the per-key-block sums.  Each block
+// sum is finished by one exchange between the two half-waves: a lane keeps
+// the four-column sums of the block it stores and hands the other
+// half-wave's block to its partner, so every lane stores and no store is
+// predicated beyond the row bound.
+template <int BS, int I0>
 __device__ __forceinline__ void epilogue_interior(const GemmParams& p, f32x16_t (&acc)[2][4], int h,
-                                                  int R_lane0, int cw, int ct, int hi) {
-  const int kb0 = cw / BS;
+                                                  int R_lane0, int cw, int hi) {
+  const int kb0 = cw / BS, ct = cw / kRangeCols;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int R = R_lane0 + j * 32;
-    float mr = acc[0][j][0];
+    float mr = acc[I0][j][0];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mr = fmaxf(mr, acc[i][j][v]);
+      for (int v = 0; v < 16; ++v) mr = fmaxf(mr, acc[I0 + i][j][v]);
     float m = mr * p.scale_log2;
     m = fmaxf(m, __shfl_xor(m, 32));
     float s[2][4];
@@ -98,7 +95,7 @@ __device__ __forceinline__ void epilogue_interior(const GemmParams& p, f32x16_t 
       for (int q = 0; q < 4; ++q) {
         float acc4 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc4 += fast_exp2(acc[i][j][4 * q + r] * p.scale_log2 - m);
+        for (int r = 0; r < 4; ++r) acc4 += fast_exp2(acc[I0 + i][j][4 * q + r] * p.scale_log2 - m);
         s[i][q] = acc4;
       }
     float zsum = 0.f;
@@ -145,12 +142,13 @@ __device__ __forceinline__ void epilogue_interior(const GemmParams& p, f32x16_t 
   }
 }
 
-// Epilogue of a diagonal or ragged wave: columns c > R (causal) or c >= Lr
-// are masked to -inf before the range max and sums.
-template <int BS>
+// Epilogue of a diagonal or ragged 64-column range: columns c > R (causal)
+// or c >= Lr are masked to -inf before the range max and sums.
+template <int BS, int I0>
 __device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&acc)[2][4], int h,
-                                                int R_lane0, int cw, int ct, int hi) {
+                                                int R_lane0, int cw, int hi) {
   const int Lr = p.Lr;
+  const int ct = cw / kRangeCols;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int R = R_lane0 + j * 32;
@@ -160,9 +158,9 @@ __device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int c = cw + i * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        float z = acc[i][j][v] * p.scale_log2;
+        float z = acc[I0 + i][j][v] * p.scale_log2;
         if (c >= Lr || (p.causal && c > R)) z = -INFINITY;
-        acc[i][j][v] = z;
+        acc[I0 + i][j][v] = z;
         m = fmaxf(m, z);
       }
     m = fmaxf(m, __shfl_xor(m, 32));
@@ -174,7 +172,7 @@ __device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&
         float acc4 = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float z = acc[i][j][4 * q + r];
+          const float z = acc[I0 + i][j][4 * q + r];
           acc4 += (z == -INFINITY) ? 0.f : fast_exp2(z - m);
         }
         s[i][q] = acc4;
@@ -186,7 +184,7 @@ __device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&
       for (int q = 0; q < 4; ++q) zsum += s[i][q];
     zsum += __shfl_xor(zsum, 32);
     // Stores are guarded rather than branched around so that every lane takes
-    // part in the exchanges below.  A wave range starting at or past Lr (the
+    // part in the exchanges below.  A range starting at or past Lr (the
     // ragged last tile) owns no snapshot slot.
     const bool row_ok = R < Lr && cw < Lr;
     const size_t rowbase = (size_t)h * p.nR32 + (R >> 5);
@@ -235,6 +233,17 @@ __device__ __forceinline__ void epilogue_masked(const GemmParams& p, f32x16_t (&
   }
 }
 
+// One 64-column range of a wave: the unmasked path where no column can be
+// masked, the masked path otherwise.
+template <int BS, int I0>
+__device__ __forceinline__ void epilogue_range(const GemmParams& p, f32x16_t (&acc)[2][4], int h, int Rw,
+                                               int cw, int l32, int hi) {
+  if (cw + kRangeCols <= p.Lr && (!p.causal || cw + kRangeCols - 1 <= Rw))
+    epilogue_interior<BS, I0>(p, acc, h, Rw + l32, cw, hi);
+  else if (!p.causal || cw <= Rw + kWaveR - 1)
+    epilogue_masked<BS, I0>(p, acc, h, Rw + l32, cw, hi);
+}
+
 // Tile of work item w: work order (kv group, tile, query head within group),
 // heads fastest; causal tiles are the lower triangle, row tr holding column
 // tiles 0 .. tr.
@@ -259,24 +268,32 @@ __device__ __forceinline__ TileItem decode_item(const GemmParams& p, int w) {
   return TileItem{g * p.group + hh, g, tr * kTileR, tc * kTileC};
 }
 
-// Persistent scoring GEMM.  Workgroups are dealt round-robin to the XCDs, so
-// workgroup b runs on XCD b % 8; XCD x owns the work items
-// [x * per_xcd, (x + 1) * per_xcd) and its wg_per_xcd workgroups (one per
-// CU) take every wg_per_xcd-th of them, so at any time one XCD's CUs work on
-// consecutive items -- a few column tiles of one tile row for all query
-// heads of one KV group -- and share their Q and K rows through its L2.
-// The copy pipeline runs across items: the last three chunk steps of an
-// item already copy the next item's first three chunks, which land while
-// the item's epilogue runs.
+// Persistent scoring GEMM: one workgroup of eight waves per CU (two per
+// SIMD), each wave owning a 64 x 128 block of the 256 x 256 tile (eight MFMA
+// accumulators).
+//
+// Scheduling: workgroups are dealt round-robin to the XCDs, so workgroup b
+// runs on XCD b % 8; XCD x owns the work items [x * per_xcd, (x+1) * per_xcd)
+// and its wg_per_xcd workgroups take every wg_per_xcd-th of them, so one
+// XCD's CUs work on consecutive items -- a few column tiles of one tile row
+// for all query heads of one KV group -- and share Q and K rows in its L2.
+//
+// Data movement: a chunk is 64 elements of S*d (four k-steps of 16), one
+// 128-byte segment of each of the tile's 512 reshaped rows -- whole cache
+// lines, which the L2 serves at twice the rate of half lines.  Two LDS
+// stages of 64 KB: chunk kc+2 is copied into chunk kc's stage once every
+// wave has read it, while chunk kc+1 is being multiplied.  The fragments of
+// the next k-step are read from LDS while the MFMAs of the current one run,
+// also across the chunk barrier, so LDS latency is hidden inside the wave.
+// The copy sequence runs across items: an item's last two chunk steps copy
+// the next item's first two chunks, which land while its epilogue runs.
 template <int D, int BS, bool PATTERN>
 __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
-  static_assert(kDmaPerWave == 4, "wait_next_chunk assumes four copies per wave per chunk");
-  // Four LDS stages as distinct objects (the chunk loop is unrolled by four)
-  // so LDS reads of one stage never wait on the direct-to-LDS copies into another.
+  static_assert(kDmaPerWave == 8 && kDmaK == 4, "copy layout assumes 8 copies per wave per chunk");
+  // Two LDS stages as distinct objects (the chunk loop is unrolled by two) so
+  // LDS reads of one stage never wait on the direct-to-LDS copies into the other.
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
 
   const int xcd = blockIdx.x % kNumXcd, slot = blockIdx.x / kNumXcd;
   const int first = xcd * p.per_xcd + slot;
@@ -297,23 +314,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
 
   // Direct-to-LDS copies through buffer resources (buffer_load ... lds).  A
   // stage holds kTileC key rows then kTileR query rows; copy n (1 KB) fills
-  // rows 16n .. 16n+15, lane -> row 16n + lane/4 and piece lane % 4.  Each
-  // lane's byte offset is fixed per item (no address register is rewritten
-  // while copies from it are in flight: the next item's offsets live in their
-  // own registers); the chunk only moves the scalar offset.  Rows past Lr
-  // (ragged last tile) re-read row Lr-1: finite data whose products are
-  // masked or never stored.
-  // Copy source of one item: its query head, KV group and the per-lane byte
-  // offsets of its rows (the chunk adds a scalar offset).
+  // rows 8n .. 8n+7, lane -> row 8n + lane/8 and 16-byte slot lane % 8, which
+  // receives the piece the swizzle places there.  Per lane the byte offset of
+  // its row is fixed per item; the chunk moves only the scalar offset.  Rows
+  // past Lr (ragged last tile) re-read row Lr-1: finite data whose products
+  // are masked or never stored.
   auto row_offsets = [&](const TileItem& t, uint32_t (&off)[kDmaPerWave]) __attribute__((always_inline)) {
 #pragma unroll
     for (int k = 0; k < kDmaPerWave; ++k) {
       const int n = k * kWaves + wave;
-      const int row = n * 16 + (lane >> 2);
-      const int piece = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = n * kRowsPerCopy + (lane >> 3);
+      const int piece = piece_slot(row, lane & 7);   // the swizzle is an involution
       if (k < kDmaK) {   // copies 0 .. kDmaK-1 of every wave cover the key rows
         const int C = min(t.C0 + row, Lr - 1);
-        off[k] = (uint32_t)(C * p.S * D * 2 + piece * 16);
+        off[k] = (uint32_t)(C * F * 2 + piece * 16);
       } else {
         const int R = min(t.R0 + row - kTileC, Lr - 1);
         off[k] = (uint32_t)(R * F * 2 + piece * 16);
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
     }
   };
   const int nk = F / kKC;
-  const int nkp = (nk + 3) & ~3;   // chunk steps per item (steps past nk reload chunk nk-1)
+  const int nkp = (nk + 1) & ~1;   // chunk steps per item (a step past nk reloads chunk nk-1)
   auto issue = [&](int h_, int g_, const uint32_t (&off)[kDmaPerWave], int kc, uint8_t* stage)
                    __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -345,35 +359,40 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
     }
   };
 
-  // fragment offsets: A = key rows 64wc + 32i + l32, B = query rows
-  // 128wr + 32j + l32; both swizzles depend on l32 only
-  int aoff[2], boff[2];
+  // Fragment offsets: A = key rows 128wc + 32i + l32, B = query rows
+  // 128wr + 32j + l32, piece 2ks + hi of the chunk; the swizzle depends on
+  // l32 only, so block i (j) adds 32 rows = 4 KB.
+  int aoff[4], boff[4];   // per k-step
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    aoff[ks] = chunk_off(wc * 64 + l32, 2 * ks + hi);
-    boff[ks] = kTileC * 64 + chunk_off(wr * kWaveRows + l32, 2 * ks + hi);
+  for (int ks = 0; ks < 4; ++ks) {
+    aoff[ks] = (wc * kWaveC + l32) * kRowBytes + piece_slot(l32, 2 * ks + hi) * 16;
+    boff[ks] = (kTileC + wr * kWaveR + l32) * kRowBytes + piece_slot(l32, 2 * ks + hi) * 16;
   }
 
   f32x16_t acc[2][4];
-  auto compute = [&](const uint8_t* stage) __attribute__((always_inline)) {
-    // all fragments of the chunk are read before the first MFMA, so one LDS
-    // latency is exposed per chunk instead of one per k-step
-    bf16x8_t af[2][2], bfr[2][4];
+  struct Frags {
+    bf16x8_t a[2], b[4];
+  };
+  auto read = [&](const uint8_t* stage, int ks, Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int i = 0; i < 2; ++i) f.a[i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * kRowBytes));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[ks][i] = as_bf16x8(*(const u32x4_t*)(stage + aoff[ks] + i * 32 * 64));
+    for (int j = 0; j < 4; ++j) f.b[j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * kRowBytes));
+  };
+  auto mma = [&](const Frags& f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[ks][j] = as_bf16x8(*(const u32x4_t*)(stage + boff[ks] + j * 32 * 64));
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(f.a[i], f.b[j], acc[i][j]);
+  };
+  // the six LDS reads of a k-step are spread over its first six MFMAs
+  auto interleave = []() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one DS read
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(af[ks][i], bfr[ks][j], acc[i][j]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // 12 DS reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // then the 16 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   };
 
   TileItem it = decode_item(p, first);
@@ -383,51 +402,60 @@ __global__ __launch_bounds__(kWaves * 64, 1) void score_gemm(GemmParams p) {
   row_offsets(it, cur_off);
   row_offsets(nx, nxt_off);
   int cur_h = it.h, cur_g = it.g, nxt_h = nx.h, nxt_g = nx.g;
-  // One chunk step kc of the current item: copy step kc+3 into the stage read
-  // in step kc-1 (every wave is past the barrier that followed it), multiply
-  // chunk kc, wait until step kc+1 has landed, synchronise.  Step kc+3 is a
-  // chunk of this item, or in the item's last three steps one of the next
-  // item's first three chunks.
-  auto step = [&](int kc, bool live, bool to_next, const uint8_t* cur_st, uint8_t* refill)
-                  __attribute__((always_inline)) {
-    if (to_next) issue(nxt_h, nxt_g, nxt_off, kc + 3 - nkp, refill);
-    else issue(cur_h, cur_g, cur_off, kc + 3, refill);
-    if (live && kc < nk) compute(cur_st);
-    wait_next_chunk();
+
+  Frags f0, f1;
+  // Chunk kc of the current item in stage `cur` (f0 holds its first k-step):
+  // k-steps 0..2 with the next k-step's fragments read alongside; then wait
+  // until this wave's reads of the stage and copies of chunk kc+1 are done and
+  // synchronise; copy chunk kc+2 (of this item, or in its last two steps one
+  // of the next item's first two chunks) into `cur`; read chunk kc+1's first
+  // k-step from `oth` alongside k-step 3.
+  auto chunk = [&](int kc, bool live, bool to_next, uint8_t* cur, const uint8_t* oth)
+                   __attribute__((always_inline)) {
+    const bool comp = live && kc < nk;
+    if (comp) {
+      read(cur, 1, f1);
+      mma(f0);
+      interleave();
+      read(cur, 2, f0);
+      mma(f1);
+      interleave();
+      read(cur, 3, f1);
+      mma(f0);
+      interleave();
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
+    if (to_next) issue(nxt_h, nxt_g, nxt_off, kc + 2 - nkp, cur);
+    else issue(cur_h, cur_g, cur_off, kc + 2, cur);
+    read(oth, 0, f0);
+    if (comp) {
+      mma(f1);
+      interleave();
+    }
   };
   issue(cur_h, cur_g, cur_off, 0, st0);
   issue(cur_h, cur_g, cur_off, 1, st1);
-  issue(cur_h, cur_g, cur_off, 2, st2);
-  wait_next_chunk();
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // chunk 0 landed
   __builtin_amdgcn_s_barrier();
+  read(st0, 0, f0);
   for (int k = 0; k < nitems; ++k) {
     // a wave whose whole column range lies right of its last row is fully masked
-    const bool live = !p.causal || (it.C0 + wc * kWaveCols <= it.R0 + wr * kWaveRows + kWaveRows - 1);
+    const bool live = !p.causal || (it.C0 + wc * kWaveC <= it.R0 + wr * kWaveR + kWaveR - 1);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
-    for (int kc = 0; kc < nkp - 4; kc += 4) {
-      step(kc, live, false, st0, st3);
-      step(kc + 1, live, false, st1, st0);
-      step(kc + 2, live, false, st2, st1);
-      step(kc + 3, live, false, st3, st2);
+    for (int kc = 0; kc < nkp - 2; kc += 2) {
+      chunk(kc, live, false, st0, st1);
+      chunk(kc + 1, live, false, st1, st0);
     }
-    step(nkp - 4, live, false, st0, st3);
-    step(nkp - 3, live, true, st1, st0);
-    step(nkp - 2, live, true, st2, st1);
-    step(nkp - 1, live, true, st3, st2);
+    chunk(nkp - 2, live, true, st0, st1);
+    chunk(nkp - 1, live, true, st1, st0);
     if (live) {
-      const int cw = it.C0 + wc * kWaveCols;   // first column of this wave's range
-      const int ct = cw / kWaveCols;
-      const int Rw = it.R0 + wr * kWaveRows;   // first row of this wave
-      // Interior waves (every column valid and, if causal, at or left of the
-      // wave's first row) need no mask.
-      if (cw + kWaveCols <= Lr && (!p.causal || cw + kWaveCols - 1 <= Rw))
-        epilogue_interior<BS>(p, acc, it.h, Rw + l32, cw, ct, hi);
-      else
-        epilogue_masked<BS>(p, acc, it.h, Rw + l32, cw, ct, hi);
+      const int cw = it.C0 + wc * kWaveC;   // first column of the wave's two ranges
+      const int Rw = it.R0 + wr * kWaveR;   // first row of the wave
+      epilogue_range<BS, 0>(p, acc, it.h, Rw, cw, l32, hi);
     }
     it = nx;
     cur_h = nxt_h;
@@ -463,7 +491,7 @@ __device__ __forceinline__ void row_stats(const float* M, const float* Z, int r,
   int nct_r = nct;
   if (causal) {
     const int last = (R / bs + 1) * bs - 1;   // last row of R's query block
-    nct_r = min(nct, last / kWaveCols + 1);
+    nct_r = min(nct, last / kRangeCols + 1);
   }
   float m = -INFINITY;
   if (R < Lr) {
@@ -492,7 +520,7 @@ __device__ __forceinline__ void row_stats(const float* M, const float* Z, int r,
 template <int BS>
 __device__ __forceinline__ float block_score(const float* P, const float* M, const float* s_mfin,
                                              const float* s_invz, int kb, int r0) {
-  const int c = (kb * BS) / kWaveCols;
+  const int c = (kb * BS) / kRangeCols;
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < BS; ++u) {
@@ -641,7 +669,7 @@ WsLayout ws_layout(const Shape& s, int S, int B) {
   w.Lr = s.L / S;
   w.NB = s.L / B;
   w.nR32 = (w.Lr + 31) / 32;
-  w.nct = (w.Lr + kWaveCols - 1) / kWaveCols;
+  w.nct = (w.Lr + kRangeCols - 1) / kRangeCols;
   w.p_elems = (size_t)s.hq * w.nR32 * w.NB * 32;
   w.m_elems = (size_t)s.hq * w.nR32 * w.nct * 32;
   return w;
