@@ -2,14 +2,18 @@
 // Sparse Attention with Antidiagonal Scoring", papercache.org summary,
 // section 1 step 3: attention computed on the selected blocks only).
 //
-// One workgroup per (query head, query block of B rows); each of its B/32
-// waves owns 32 query rows.  The key/value blocks to visit -- the selected
-// ones in sparse mode, all causal-visible ones in dense mode -- stream
-// through LDS in tiles of 64 keys, double buffered: while a tile is being
-// used, the next one is copied global -> LDS by direct-to-LDS loads, so the
-// copy never passes through registers.  K and V tiles are stored row-major
-// with an XOR swizzle of their 16-byte chunks (conflict-free reads for both
-// access patterns below).
+// One workgroup per (query head, pair of neighbouring query blocks of B rows
+// each); each of its 2B/32 waves owns 32 query rows of one of the two
+// blocks.  The key/value blocks to visit -- the union of the two blocks'
+// selected sets in sparse mode, all causal-visible ones in dense mode --
+// stream through LDS in tiles of 64 keys, double buffered: while a tile is
+// being used, the next one is copied global -> LDS by direct-to-LDS loads, so
+// the copy never passes through registers.  Each tile is copied
+// once for both blocks; a wave skips the tiles its own block does not use
+// (neighbouring blocks select largely the same keys, so the copy traffic per
+// query row falls by about 40 % against one block per workgroup).  K and V
+// tiles are stored row-major with an XOR swizzle of their 16-byte chunks
+// (conflict-free reads for both access patterns below).
 //
 // Per tile a wave computes S^T = K Q^T with 32x32x16 bf16 MFMAs (each lane
 // then owns one query row), applies the causal mask, an online softmax in the
@@ -95,8 +99,10 @@ __device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
 }
 
 template <int D, int BQ>
-__global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
-  constexpr int kWaves = BQ / 32;
+__global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
+  constexpr int kBlockWaves = BQ / 32;          // waves per query block
+  constexpr int kWaves = 2 * kBlockWaves;        // a workgroup covers two query blocks
+  constexpr int kThreads = kWaves * 64;
   constexpr int kTilesPerBlock = BQ / kKT;
   constexpr int kTileBytes = kKT * D * 2;
   // Two K/V buffers as distinct objects: with the loop unrolled by two every
@@ -107,15 +113,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
 
-  // Work order.  Items of one KV group are (query block descending, head),
-  // cut into chunks of 4 query blocks x all heads of the group.  Chunks are
-  // dealt round-robin to the 8 XCDs and every XCD runs through the groups in
-  // the same order, so (a) all XCDs work on the same KV group at a time -- its
+
+  // Work order.  A work item is a pair of neighbouring query blocks (2i,
+  // 2i+1) of one head.  Items of one KV group are (pair descending, head),
+  // cut into chunks of 4 pairs x all heads of the group.  Chunks are dealt
+  // round-robin to the 8 XCDs and every XCD runs through the groups in the
+  // same order, so (a) all XCDs work on the same KV group at a time -- its
   // K/V stays resident in the memory-side cache -- and (b) the work-groups on
   // one XCD share neighbouring query blocks and all heads of the group in its
   // L2.  When the counts do not divide evenly, each XCD takes a contiguous
   // range instead (one KV group per XCD).
-  const int per_group = p.NB * p.group;
+  const int npairs = (p.NB + 1) / 2;
+  const int per_group = npairs * p.group;
   int g, rem;
   if (p.interleave) {
     const int bid = blockIdx.x;
@@ -132,15 +141,23 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
     g = w / per_group;
     rem = w % per_group;
   }
-  const int qb = p.NB - 1 - rem / p.group;
+  const int pair = npairs - 1 - rem / p.group;
   const int h = g * p.group + rem % p.group;
+  // Waves 0 .. kBlockWaves-1 take query block qbA, the others qbB (== NB when
+  // NB is odd and this is the last pair: those waves only help copy).  Wave w
+  // runs on SIMD w % 4, so each SIMD holds one wave of each block.
+  const int qbA = 2 * pair, qbB = 2 * pair + 1;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int qrow = qb * BQ + wave * 32 + l32;   // this lane's query token
-  const int qwave0 = qb * BQ + wave * 32;
+  const int half = wave / kBlockWaves;           // 0: block A, 1: block B
+  const int qb = qbA + half;
+  const bool rows_valid = qb < p.NB;
+  const int wq = wave % kBlockWaves;
+  const int qrow = qb * BQ + wq * 32 + l32;      // this lane's query token
+  const int qwave0 = qb * BQ + wq * 32;
 
   const uint16_t* Kg = p.K + (size_t)g * p.L * D;
   const uint16_t* Vg = p.V + (size_t)g * p.L * D;
@@ -148,30 +165,80 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   // query fragments (B operand of S^T = K Q^T): lane holds Q[qrow][16t + 8hi .. +8]
   bf16x8_t qf[D / 16];
   {
-    const uint16_t* qp = p.Q + ((size_t)h * p.L + qrow) * D + hi * 8;
+    const uint16_t* qp = p.Q + ((size_t)h * p.L + (rows_valid ? qrow : qrow - BQ)) * D + hi * 8;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qp + 16 * t));
   }
 
-  // Sparse mode: the workgroup's block list is staged in LDS once, so the
-  // per-tile lookup is an LDS read rather than a global-memory round trip.
-  extern __shared__ int32_t s_list[];
+  // The key blocks the workgroup visits: the union of the two blocks' sets,
+  // in ascending order, each with a flag per block.  Sparse mode builds it in
+  // LDS from the two lists (as bitmaps: invalid entries dropped, a repeated
+  // entry kept once); dense mode visits every causal-visible block.
+  extern __shared__ int32_t s_dyn[];
+  const int nw32 = (p.NB + 31) / 32;
+  int32_t* s_list = s_dyn;                                  // [NB]: kb | flagA << 30 | flagB << 31
+  uint32_t* s_bits = (uint32_t*)(s_dyn + p.NB);             // [2][nw32]
+  int32_t* s_off = s_dyn + p.NB + 2 * nw32;                 // [nw32 + 1]
   int nkb;
   const bool sparse = p.idx != nullptr;
   if (sparse) {
-    nkb = p.counts[(size_t)h * p.NB + qb];
-    nkb = nkb < 0 ? 0 : (nkb > p.NB ? p.NB : nkb);
-    const int32_t* list = p.idx + ((size_t)h * p.NB + qb) * p.NB;
-    for (int j = tid; j < nkb; j += BQ * 2) s_list[j] = list[j];
+    for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int qbb = qbA + b;
+      if (qbb >= p.NB) continue;
+      int cnt = p.counts[(size_t)h * p.NB + qbb];
+      cnt = cnt < 0 ? 0 : (cnt > p.NB ? p.NB : cnt);
+      const int32_t* list = p.idx + ((size_t)h * p.NB + qbb) * p.NB;
+      for (int j = tid; j < cnt; j += kThreads) {
+        const int kb = list[j];
+        if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) continue;
+        atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int acc = 0;
+      for (int w = 0; w < nw32; ++w) {
+        s_off[w] = acc;
+        acc += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
+      }
+      s_off[nw32] = acc;
+    }
+    __syncthreads();
+    for (int w = tid; w < nw32; w += kThreads) {
+      const uint32_t a = s_bits[w], bb = s_bits[nw32 + w];
+      uint32_t u = a | bb;
+      int o = s_off[w];
+      while (u) {
+        const int bit = __builtin_ctz(u);
+        s_list[o++] = (int32_t)((uint32_t)(32 * w + bit) | (((a >> bit) & 1u) << 30) | (((bb >> bit) & 1u) << 31));
+        u &= u - 1;
+      }
+    }
+    nkb = s_off[nw32];
     __syncthreads();
   } else {
-    nkb = p.causal ? qb + 1 : p.NB;
+    nkb = p.causal ? min(qbB, p.NB - 1) + 1 : p.NB;
   }
   const int ntiles = nkb * kTilesPerBlock;
-  auto tile_key0 = [&](int n) -> int {   // first key of tile n, or -1 to skip it
+  // first key of tile n and whether this wave's query block uses it
+  auto tile_info = [&](int n, bool& mine) -> int {
     const int j = n / kTilesPerBlock;
-    const int kb = sparse ? __builtin_amdgcn_readfirstlane(s_list[j]) : j;
-    if (kb < 0 || kb >= p.NB || (p.causal && kb > qb)) return -1;
+    int kb;
+    bool fa, fb;
+    if (sparse) {
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_list[j]);
+      kb = (int)(e & 0x3FFFFFFFu);
+      fa = (e >> 30) & 1u;
+      fb = e >> 31;
+    } else {
+      kb = j;
+      fa = !p.causal || kb <= qbA;
+      fb = qbB < p.NB && (!p.causal || kb <= qbB);
+    }
+    mine = half ? fb : fa;
     return kb * BQ + (n % kTilesPerBlock) * kKT;
   };
 
@@ -199,7 +266,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
         voff[dt][r] = tile_off<D>(vrow + 8 * r, 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3));
   }
 
-  int key0 = ntiles > 0 ? tile_key0(0) : -1;
+  bool mine = false;
+  int key0 = ntiles > 0 ? tile_info(0, mine) : -1;
   if (key0 >= 0) {
     load_tile<D, kWaves>(Kg, key0, sK0, wave, lane);
     load_tile<D, kWaves>(Vg, key0, sV0, wave, lane);
@@ -211,12 +279,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   // wait for the copy and synchronise.
   auto step = [&](int n, const uint8_t* sK, const uint8_t* sV, uint8_t* nK,
                   uint8_t* nV) __attribute__((always_inline)) {
-    const int key0_next = (n + 1 < ntiles) ? tile_key0(n + 1) : -1;
+    bool mine_next = false;
+    const int key0_next = (n + 1 < ntiles) ? tile_info(n + 1, mine_next) : -1;
     if (key0_next >= 0) {
       load_tile<D, kWaves>(Kg, key0_next, nK, wave, lane);
       load_tile<D, kWaves>(Vg, key0_next, nV, wave, lane);
     }
-    if (key0 >= 0 && !(p.causal && key0 > qwave0 + 31)) {
+    if (key0 >= 0 && mine && !(p.causal && key0 > qwave0 + 31)) {
       // S^T (64 keys x 32 queries) as two 32x32 tiles.  K fragments are read
       // kAhead k-steps before their MFMAs so LDS latency overlaps the matrix
       // work instead of stalling each MFMA.
@@ -312,6 +381,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
       }
     }
     key0 = key0_next;
+    mine = mine_next;
     wait_vmem();
     __syncthreads();
   };
@@ -321,6 +391,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
   }
 
   // normalise and store: lane holds O[qrow][32 dt + 8 gg + 4 hi + r]
+  if (!rows_valid) return;
   const float ltot = lsum + __shfl_xor(lsum, 32);
   const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
   uint16_t* op = p.O + ((size_t)h * p.L + qrow) * D;
@@ -338,8 +409,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void flash_bf16_kernel(FlashParams p) {
 
 template <int D, int BQ>
 hipError_t launch(const FlashParams& fp, hipStream_t st) {
-  const size_t list_bytes = fp.idx ? (size_t)fp.NB * sizeof(int32_t) : 0;
-  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 2), list_bytes, st, fp);
+  const int nw32 = (fp.NB + 31) / 32;
+  const size_t list_bytes = fp.idx ? (size_t)(fp.NB + 3 * nw32 + 1) * sizeof(int32_t) : 0;
+  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 4), list_bytes, st, fp);
   return hipGetLastError();
 }
 
@@ -360,9 +432,10 @@ hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const
   fp.group = s.hq / s.hkv;
   fp.NB = s.L / B;
   fp.causal = s.causal;
-  fp.nwork = fp.NB * s.hq;
+  const int npairs = (fp.NB + 1) / 2;
+  fp.nwork = npairs * s.hq;
   fp.grid = (fp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
-  fp.interleave = (fp.NB * fp.group) % (kNumXcd * 4 * fp.group) == 0;
+  fp.interleave = (npairs * fp.group) % (kNumXcd * 4 * fp.group) == 0;
   fp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
   if (s.d == 128) return B == 128 ? launch<128, 128>(fp, st) : launch<128, 64>(fp, st);
   return B == 128 ? launch<64, 128>(fp, st) : launch<64, 64>(fp, st);

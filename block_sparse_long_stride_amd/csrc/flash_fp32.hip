@@ -42,18 +42,8 @@ __global__ __launch_bounds__(256) void flash_fp32_kernel(Fp32FlashParams p) {
   }
   float m = -INFINITY, l = 0.f;
 
-  int nkb;
-  const int32_t* list = nullptr;
-  if (p.idx) {
-    nkb = p.counts[(size_t)h * p.NB + qb];
-    nkb = nkb < 0 ? 0 : (nkb > p.NB ? p.NB : nkb);
-    list = p.idx + ((size_t)h * p.NB + qb) * p.NB;
-  } else {
-    nkb = p.causal ? qb + 1 : p.NB;
-  }
-  for (int j = 0; j < nkb; ++j) {
-    const int kb = list ? list[j] : j;
-    if (kb < 0 || kb >= p.NB || (p.causal && kb > qb)) continue;   // uniform per block
+  // One key block: stream its keys through LDS and update the online softmax.
+  auto visit = [&](int kb) {
     for (int t0 = 0; t0 < p.B; t0 += kKT) {
       const int nk = min(kKT, p.B - t0);
       const int key0 = kb * p.B + t0;
@@ -79,6 +69,33 @@ __global__ __launch_bounds__(256) void flash_fp32_kernel(Fp32FlashParams p) {
         m = mnew;
       }
     }
+  };
+  if (p.idx) {
+    // The list as a set: a bitmap in LDS (invalid entries dropped, repeats
+    // kept once), walked in ascending block order by the whole workgroup.
+    extern __shared__ uint32_t s_bits[];
+    const int nw32 = (p.NB + 31) / 32;
+    for (int w = tid; w < nw32; w += blockDim.x) s_bits[w] = 0u;
+    __syncthreads();
+    int cnt = p.counts[(size_t)h * p.NB + qb];
+    cnt = cnt < 0 ? 0 : (cnt > p.NB ? p.NB : cnt);
+    const int32_t* list = p.idx + ((size_t)h * p.NB + qb) * p.NB;
+    for (int j = tid; j < cnt; j += blockDim.x) {
+      const int kb = list[j];
+      if (kb < 0 || kb >= p.NB || (p.causal && kb > qb)) continue;
+      atomicOr(&s_bits[kb >> 5], 1u << (kb & 31));
+    }
+    __syncthreads();
+    for (int w = 0; w < nw32; ++w) {
+      uint32_t bits = s_bits[w];
+      while (bits) {
+        visit(32 * w + __builtin_ctz(bits));
+        bits &= bits - 1;
+      }
+    }
+  } else {
+    const int nkb = p.causal ? qb + 1 : p.NB;
+    for (int kb = 0; kb < nkb; ++kb) visit(kb);
   }
   if (!live) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -89,7 +106,8 @@ __global__ __launch_bounds__(256) void flash_fp32_kernel(Fp32FlashParams p) {
 template <int D>
 hipError_t launch(const Fp32FlashParams& fp, int hq, hipStream_t st) {
   const int threads = (fp.B + 63) / 64 * 64;
-  hipLaunchKernelGGL((flash_fp32_kernel<D>), dim3(hq * fp.NB), dim3(threads), 0, st, fp);
+  const size_t bitmap_bytes = fp.idx ? (size_t)((fp.NB + 31) / 32) * sizeof(uint32_t) : 0;
+  hipLaunchKernelGGL((flash_fp32_kernel<D>), dim3(hq * fp.NB), dim3(threads), bitmap_bytes, st, fp);
   return hipGetLastError();
 }
 

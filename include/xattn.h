@@ -223,7 +223,9 @@ xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, in
  *
  *   idx, counts  in, as written by xattn_select.  Entries outside [0, NB)
  *                and, when causal, entries > qb are ignored; counts are
- *                clamped to [0, NB].  A row with no key gets O = 0.
+ *                clamped to [0, NB].  The list is a set of blocks: a repeated
+ *                entry counts once and blocks are visited in ascending
+ *                order.  A row with no key gets O = 0.
  *   O            out, [hq][L][d] in the input dtype, fully overwritten.
  * Requires L % B == 0.  bf16 kernels cover d in {64, 128}, B in {64, 128};
  * fp32 kernels cover d <= 128, B <= 256.

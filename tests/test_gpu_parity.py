@@ -251,7 +251,9 @@ def test_tau_one_selects_every_block_and_matches_full(name):
 @pytest.mark.parametrize("name", ["llm-S8-B128", "c1-fp32"])
 def test_sparse_prefill_edge_lists(name):
     """Empty lists give zeros; invalid entries (-1, >= NB, > qb when causal)
-    are ignored; a single block equals attention over that block alone."""
+    are ignored; a single block equals attention over that block alone; a list
+    is a set (repeated or descending entries give the attention over the
+    distinct blocks)."""
     import torch
     from block_sparse_long_stride_amd import xattn_sparse_prefill
     cfg, w, dev, ora = case(name)
@@ -262,7 +264,7 @@ def test_sparse_prefill_edge_lists(name):
     expect_lists = {}
     for h in range(cfg.hq):
         for qb in range(NB):
-            mode = (h * NB + qb) % 4
+            mode = (h * NB + qb) % 5
             if mode == 0:
                 lst, cnt = [], 0
             elif mode == 1:
@@ -272,8 +274,12 @@ def test_sparse_prefill_edge_lists(name):
                 kb = int(rng.integers(0, qb + 1))
                 lst = [-5, kb, NB + 3, min(qb + 1, NB - 1) if qb + 1 < NB else -1]
                 cnt = len(lst)
-            else:             # count larger than NB is clamped; entries after are -1
+            elif mode == 3:   # count larger than NB is clamped; entries after are -1
                 lst, cnt = [qb], NB + 7
+            else:             # repeats in descending order
+                a, b = (int(x) for x in rng.integers(0, qb + 1, size=2))
+                lst = [max(a, b), min(a, b), max(a, b), min(a, b)]
+                cnt = len(lst)
             idx[h, qb, :len(lst)] = lst
             counts[h, qb] = cnt
             valid = [k for k in lst[:min(cnt, NB)] if 0 <= k < NB and (not cfg.causal or k <= qb)]
