@@ -26,6 +26,9 @@ SMALL = {
     "llm-d64-B64": get_config(2, hq=2, hkv=1, L=2048, d=64, B=64, S=8),
     "llm-d64-tau-range": get_config(4, hq=4, hkv=2, L=4096, d=64),
     "video-ragged": get_config(5, hq=2, hkv=2, frames=3),
+    # causal, odd number of query blocks (33: the last pair of blocks has one)
+    # and L/S = 528, a ragged last scoring tile
+    "llm-odd-blocks": get_config(2, hq=2, hkv=1, L=4224),
     "noncausal-llm-fp32": get_config(1, causal=False, L=1024),
 }
 
