@@ -515,19 +515,25 @@ __device__ __forceinline__ void row_stats(const float* M, const float* Z, int r,
 
 // Block score of key block kb for the query block whose reshaped rows are
 // r0 .. r0+BS-1 of the group: the rows' partial block sums rescaled to the
-// rows' final softmax, summed in row order, divided by BS.  The BS row loads
-// are independent and issued together.
+// rows' final softmax, summed in row order, divided by BS.
 template <int BS>
 __device__ __forceinline__ float block_score(const float* P, const float* M, const float* s_mfin,
                                              const float* s_invz, int kb, int r0) {
   const int c = (kb * BS) / kRangeCols;
+  // the BS partial sums and range maxima of the block's rows: BS/4 16-byte
+  // loads each (r0 is a multiple of BS >= 4, rows of 32 floats)
+  f32x4_t pv[BS / 4], mv[BS / 4];
+#pragma unroll
+  for (int g = 0; g < BS / 4; ++g) {
+    pv[g] = *(const f32x4_t*)(P + (size_t)kb * 32 + r0 + 4 * g);
+    mv[g] = *(const f32x4_t*)(M + c * 32 + r0 + 4 * g);
+  }
   float acc = 0.f;
 #pragma unroll
   for (int u = 0; u < BS; ++u) {
     const int r = r0 + u;
-    const float mc = M[c * 32 + r];
-    const float pv = P[(size_t)kb * 32 + r];
-    if (mc != -INFINITY) acc += pv * fast_exp2(mc - s_mfin[r]) * s_invz[r];
+    const float mc = mv[u / 4][u % 4];
+    if (mc != -INFINITY) acc += pv[u / 4][u % 4] * fast_exp2(mc - s_mfin[r]) * s_invz[r];
   }
   return acc * (1.0f / (float)BS);
 }
