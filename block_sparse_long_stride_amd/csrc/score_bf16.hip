@@ -595,7 +595,6 @@ struct FusedParams {
 
 template <int CAP, int BS>
 __global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams p) {
-  __shared__ SelectScratch<CAP> sh;
   __shared__ float s_row[CAP];
   __shared__ float s_mfin[32];
   __shared__ float s_invz[32];
@@ -625,10 +624,11 @@ __global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams
     s_row[kb] = (!p.causal || kb <= qb) ? block_score<BS>(P, M, s_mfin, s_invz, kb, r0)
                                         : 0.f;
   __syncthreads();
+  if (tid >= 64) return;
   const CutSpec cut{kThreshold, 0, 0.f, p.tau.v[h]};
-  rank_and_cut<CAP>(sh, [&](int i) { return s_row[i]; }, p.causal ? qb + 1 : p.NB, p.NB,
-                    p.nwords, cut, p.mask + (size_t)row * p.nwords, p.idx + (size_t)row * p.NB,
-                    p.counts + row);
+  rank_and_cut<CAP / 64>([&](int i) { return s_row[i]; }, p.causal ? qb + 1 : p.NB, p.NB,
+                         p.nwords, cut, p.mask + (size_t)row * p.nwords,
+                         p.idx + (size_t)row * p.NB, p.counts + row);
 }
 
 template <int D, int BS>

@@ -1,13 +1,14 @@
 // Threshold block selection: find_blocks(A, tau) ("XAttention: Block Sparse
 // Attention with Antidiagonal Scoring", papercache.org summary, section 2.2;
-// chapterpal.com Knowl 2).  One workgroup per (head, query block).
+// chapterpal.com Knowl 2).  One wavefront per (head, query block), four rows
+// per workgroup.
 //
 // The smallest set of key blocks whose score sum reaches tau is a prefix of
-// the blocks ranked by score.  The kernel ranks the valid blocks with an LDS
-// bitonic sort of 64-bit keys (order-preserving score bits, then the inverted
-// block id, so equal scores keep the lower block first), forms the prefix sums
-// of the ranked scores in float64, cuts at the first prefix >= tau, and emits
-// the bitmask, the ascending block ids (padded with -1) and the count.
+// the blocks ranked by score (descending; equal scores keep the lower block
+// first), and the first prefix whose float64 sum is >= tau ends it.  The
+// wave finds where that prefix ends without sorting the row (a bitwise
+// search over the score keys, select_row.h) and emits the bitmask, the
+// ascending block ids (padded with -1) and the count.
 //
 // The same kernel serves the two fixed-count cut rules of the ablation on
 // block selection strategies (chapterpal.com Knowl 9, "Selection Strategy";
@@ -27,29 +28,32 @@ struct SelectParams {
   uint64_t* mask;
   int32_t* idx;
   int32_t* counts;
-  int NB, causal, nwords;
+  int NB, causal, nwords, rows;
   int rule;        // CutRule
   int topk;        // kTopK: blocks kept
   float ratio;     // kTopRatio: share of the valid blocks kept
   TauArray tau;    // kThreshold: per-head tau
 };
 
-template <int CAP>
+template <int EPL>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectParams p) {
-  __shared__ SelectScratch<CAP> sh;
-  const int row = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = blockIdx.x * kSelectRowsPerBlock + wave;
+  if (row >= p.rows) return;
   const int h = row / p.NB;
   const int qb = row % p.NB;
   const int n = p.causal ? qb + 1 : p.NB;
   const float* srow = p.scores + (size_t)row * p.NB;
   const CutSpec cut{p.rule, p.topk, p.ratio, p.rule == kThreshold ? p.tau.v[h] : 1.0f};
-  rank_and_cut<CAP>(sh, [&](int i) { return srow[i]; }, n, p.NB, p.nwords, cut,
+  rank_and_cut<EPL>([&](int i) { return srow[i]; }, n, p.NB, p.nwords, cut,
                     p.mask + (size_t)row * p.nwords, p.idx + (size_t)row * p.NB, p.counts + row);
 }
 
-template <int CAP>
-hipError_t launch_cap(const SelectParams& sp, int rows, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<CAP>), dim3(rows), dim3(kSelectThreads), 0, st, sp);
+template <int EPL>
+hipError_t launch_epl(SelectParams sp, int rows, hipStream_t st) {
+  sp.rows = rows;
+  const int blocks = (rows + kSelectRowsPerBlock - 1) / kSelectRowsPerBlock;
+  hipLaunchKernelGGL((select_kernel<EPL>), dim3(blocks), dim3(kSelectThreads), 0, st, sp);
   return hipGetLastError();
 }
 
@@ -67,9 +71,11 @@ SelectParams make_params(int NB, int causal, const float* scores, uint64_t* mask
 }
 
 hipError_t launch_rows(const SelectParams& sp, int rows, hipStream_t st) {
-  if (sp.NB <= 256) return launch_cap<256>(sp, rows, st);
-  if (sp.NB <= 1024) return launch_cap<1024>(sp, rows, st);
-  return launch_cap<4096>(sp, rows, st);
+  // registers per lane: NB <= 64 * EPL (NB <= kMaxSelectBlocks = 4096)
+  if (rows == 0) return hipSuccess;
+  if (sp.NB <= 256) return launch_epl<4>(sp, rows, st);
+  if (sp.NB <= 1024) return launch_epl<16>(sp, rows, st);
+  return launch_epl<64>(sp, rows, st);
 }
 
 }  // namespace
