@@ -94,6 +94,19 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// max(x[l], x[l ^ 32]) in every lane l, without the LDS crossbar:
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so two copies of x end up holding x[l] and
+// x[l ^ 32] between them.  Written as a VALU asm statement with both
+// registers read-write: this hipcc gives the builtin's second result the
+// first result's register.  The s_nop covers the wait after the VALU write of
+// the operands.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 __device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
@@ -318,6 +331,21 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // V^T fragments (A operand of O^T += V^T P^T) of 16-key chunk u and
+      // output column block dt, by transposed LDS reads; chunk 0 is read now
+      // so the reads land during the softmax.
+      auto read_v = [&](int u, int dt) -> bf16x8_t {
+        const uint8_t* vp = sV + 16 * u * D * 2;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][0]));
+        const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][1]));
+        return as_bf16x8(u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                                 __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]});
+      };
+      bf16x8_t vf[2][D / 32];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) vf[0][dt] = read_v(0, dt);
+      __builtin_amdgcn_sched_barrier(0);
       if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -332,7 +360,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * p.scale_log2;
+      mloc = max_with_other_half(mloc) * p.scale_log2;
       // The reference max m of a row only moves when this tile's max exceeds it
       // by more than kSlack (log2 units), so P stays <= 2^kSlack and the O /
       // denominator rescale (a wave-uniform branch) is rare.  The result is
@@ -348,37 +376,42 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
         m = mnew;
       }
       const float mref = (m == -INFINITY) ? 0.f : m;
-      // P in bf16; the denominator sums the same rounded values (packed dot2).
+      // P in bf16 in four chunks of 16 keys; the denominator sums the same
+      // rounded values (packed dot2, in chunk order).  The MFMAs of chunk u
+      // are interleaved with the exponentials and V reads of chunk u + 1
+      // (fenced, so the vector and matrix work of one wave overlap).
       const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
       float rs0 = 0.f, rs1 = 0.f;
-      bf16x8_t pf[4];
+      auto p_pair = [&](int u, int e) -> uint32_t {
+        const int i = u >> 1, v0 = (u & 1) * 8;
+        const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], p.scale_log2, -mref));
+        const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], p.scale_log2, -mref));
+        const uint32_t pk = cvt2_bf16(p0, p1);
+        if (e & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs1, false);
+        else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs0, false);
+        return pk;
+      };
+      constexpr int kDt = D / 32;            // output column blocks
+      constexpr int kPairsPerDt = 4 / kDt;   // P pairs of the next chunk per MFMA
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = p_pair(0, e);
+      bf16x8_t pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = u >> 1, v0 = (u & 1) * 8;
-        uint32_t pk[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], p.scale_log2, -mref));
-          const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], p.scale_log2, -mref));
-          pk[e] = cvt2_bf16(p0, p1);
-          if (e & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ones, rs1, false);
-          else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ones, rs0, false);
+        for (int dt = 0; dt < kDt; ++dt) {
+          o[dt] = mfma_32x32x16(vf[u & 1][dt], pcur, o[dt]);
+          if (u < 3) {
+            vf[(u + 1) & 1][dt] = read_v(u + 1, dt);
+#pragma unroll
+            for (int e = dt * kPairsPerDt; e < (dt + 1) * kPairsPerDt; ++e) pk[e] = p_pair(u + 1, e);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        pf[u] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        if (u < 3) pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
       }
       lsum += rs0 + rs1;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint8_t* vp = sV + 16 * u * D * 2;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][0]));
-          const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][1]));
-          const u32x4_t vv = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                              __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]};
-          o[dt] = mfma_32x32x16(as_bf16x8(vv), pf[u], o[dt]);
-        }
-      }
     }
     key0 = key0_next;
     mine = mine_next;
