@@ -577,11 +577,12 @@ __global__ __launch_bounds__(256) void score_fixup(FixupParams p) {
   }
 }
 
-// Fused finishing + threshold selection: one workgroup per (head, query
-// block) computes the block scores of its row exactly as score_fixup does --
-// same helpers, same order, so the same bits -- keeps them in LDS and ranks
-// and cuts them (rank_and_cut, as xattn_select).  The [hq][NB][NB] score
-// matrix never reaches memory.
+// Fused finishing + threshold selection: one workgroup per (head, 32
+// reshaped rows) computes the block scores of the group's 32/bs query blocks
+// exactly as score_fixup does -- same helpers, same order, so the same bits
+// -- keeps them in LDS, and each wave ranks and cuts whole rows
+// (rank_and_cut, as xattn_select).  The [hq][NB][NB] score matrix never
+// reaches memory.
 struct FusedParams {
   const float* P;
   const float* M;
@@ -593,42 +594,49 @@ struct FusedParams {
   TauArray tau;
 };
 
-template <int CAP, int BS>
-__global__ __launch_bounds__(kSelectThreads) void score_select_fused(FusedParams p) {
-  __shared__ float s_row[CAP];
+template <int EPL, int BS>
+__global__ __launch_bounds__(256) void score_select_fused(FusedParams p) {
+  extern __shared__ float s_sc[];   // [32 / BS][NB] block scores of the group's query blocks
   __shared__ float s_mfin[32];
   __shared__ float s_invz[32];
-  const int row = blockIdx.x;
-  const int h = row / p.NB, qb = row % p.NB;
+  const int h = blockIdx.x / p.nR32;
+  const int rg = blockIdx.x % p.nR32;
   const int tid = threadIdx.x;
-  const int R0 = qb * p.bs, rg = R0 / 32, r0 = R0 % 32;
   const size_t rowbase = (size_t)h * p.nR32 + rg;
   const float* M = p.M + rowbase * p.nct * 32;
   const float* Z = p.Z + rowbase * p.nct * 32;
   const float* P = p.P + rowbase * p.NB * 32;
   {
-    // rows r0 .. r0+bs-1 of the group, 8 lanes each (lanes past bs rows idle
-    // through the same code on a row past Lr)
-    const int rl = tid >> 3, sub = tid & 7;
-    const bool used = rl < p.bs;
-    const int r = r0 + (used ? rl : 0);
+    const int r = tid >> 3, sub = tid & 7;
     float m, invz;
-    row_stats(M, Z, r, used ? rg * 32 + r : p.Lr, p.Lr, p.nct, BS, p.causal, sub, m, invz);
-    if (used && sub == 0) {
+    row_stats(M, Z, r, rg * 32 + r, p.Lr, p.nct, BS, p.causal, sub, m, invz);
+    if (sub == 0) {
       s_mfin[r] = m;
       s_invz[r] = invz;
     }
   }
   __syncthreads();
-  for (int kb = tid; kb < p.NB; kb += kSelectThreads)
-    s_row[kb] = (!p.causal || kb <= qb) ? block_score<BS>(P, M, s_mfin, s_invz, kb, r0)
-                                        : 0.f;
+  constexpr int nq = 32 / BS;
+  const int qb0 = rg * nq;
+#pragma unroll 2
+  for (int it = tid; it < nq * p.NB; it += blockDim.x) {
+    const int kb = it / nq, q = it % nq;
+    const int qb = qb0 + q;
+    if (qb >= p.NB) continue;
+    s_sc[q * p.NB + kb] =
+        (!p.causal || kb <= qb) ? block_score<BS>(P, M, s_mfin, s_invz, kb, q * BS) : 0.f;
+  }
   __syncthreads();
-  if (tid >= 64) return;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const CutSpec cut{kThreshold, 0, 0.f, p.tau.v[h]};
-  rank_and_cut<CAP / 64>([&](int i) { return s_row[i]; }, p.causal ? qb + 1 : p.NB, p.NB,
-                         p.nwords, cut, p.mask + (size_t)row * p.nwords,
-                         p.idx + (size_t)row * p.NB, p.counts + row);
+  for (int q = wave; q < nq; q += 4) {
+    const int qb = qb0 + q;
+    if (qb >= p.NB) break;
+    const size_t row = (size_t)h * p.NB + qb;
+    const float* srow = s_sc + q * p.NB;
+    rank_and_cut<EPL>([&](int i) { return srow[i]; }, p.causal ? qb + 1 : p.NB, p.NB, p.nwords,
+                      cut, p.mask + row * p.nwords, p.idx + row * p.NB, p.counts + row);
+  }
 }
 
 template <int D, int BS>
@@ -723,14 +731,15 @@ hipError_t run_score_gemm(const Shape& s, const void* Q, const void* K, int S, i
   return (s.d == 128) ? launch_gemm_bs<128>(gp, bs, st) : launch_gemm_bs<64>(gp, bs, st);
 }
 
-template <int CAP>
-hipError_t launch_fused(const FusedParams& fp, int rows, hipStream_t st) {
-  const dim3 grid(rows), block(kSelectThreads);
+template <int EPL>
+hipError_t launch_fused(const FusedParams& fp, int groups, hipStream_t st) {
+  const dim3 grid(groups), block(256);
+  const size_t lds = (size_t)(32 / fp.bs) * fp.NB * sizeof(float);   // <= 8 x 4096 floats
   switch (fp.bs) {
-    case 4: hipLaunchKernelGGL((score_select_fused<CAP, 4>), grid, block, 0, st, fp); break;
-    case 8: hipLaunchKernelGGL((score_select_fused<CAP, 8>), grid, block, 0, st, fp); break;
-    case 16: hipLaunchKernelGGL((score_select_fused<CAP, 16>), grid, block, 0, st, fp); break;
-    case 32: hipLaunchKernelGGL((score_select_fused<CAP, 32>), grid, block, 0, st, fp); break;
+    case 4: hipLaunchKernelGGL((score_select_fused<EPL, 4>), grid, block, lds, st, fp); break;
+    case 8: hipLaunchKernelGGL((score_select_fused<EPL, 8>), grid, block, lds, st, fp); break;
+    case 16: hipLaunchKernelGGL((score_select_fused<EPL, 16>), grid, block, lds, st, fp); break;
+    case 32: hipLaunchKernelGGL((score_select_fused<EPL, 32>), grid, block, lds, st, fp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -788,10 +797,10 @@ hipError_t launch_score_select_bf16(const Shape& s, const void* Q, const void* K
   fp.causal = s.causal;
   fp.nwords = (wl.NB + 63) / 64;
   fp.tau = tau;
-  const int rows = s.hq * wl.NB;
-  if (wl.NB <= 256) return launch_fused<256>(fp, rows, st);
-  if (wl.NB <= 1024) return launch_fused<1024>(fp, rows, st);
-  return launch_fused<4096>(fp, rows, st);
+  const int groups = s.hq * wl.nR32;
+  if (wl.NB <= 256) return launch_fused<4>(fp, groups, st);
+  if (wl.NB <= 1024) return launch_fused<16>(fp, groups, st);
+  return launch_fused<64>(fp, groups, st);
 }
 
 }  // namespace xattn
