@@ -6,7 +6,7 @@
 // each); each of its 2B/32 waves owns 32 query rows of one of the two
 // blocks.  The key/value blocks to visit -- the union of the two blocks'
 // selected sets in sparse mode, all causal-visible ones in dense mode --
-// stream through LDS in tiles of 64 keys, double buffered: while a tile is
+// stream through LDS one block (B keys) per tile, double buffered: while a tile is
 // being used, the next one is copied global -> LDS by direct-to-LDS loads, so
 // the copy never passes through registers.  Each tile is copied
 // once for both blocks; a wave skips the tiles its own block does not use
@@ -27,7 +27,6 @@
 namespace xattn {
 namespace {
 
-constexpr int kKT = 64;   // keys per LDS tile
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -69,12 +68,17 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 // Copy one 64 x D tile (rows key0 .. key0+63 of src) into LDS by direct-to-LDS
 // loads.  Each instruction of a wave fills 1 KB of LDS in lane order; lane l
 // fetches the global chunk that the swizzled layout places at its position.
-template <int D, int NWAVES>
+// Keys per LDS tile: one whole 128-key block per step for B = 128 (half the
+// steps, barriers and per-step softmax overhead of 64-key tiles), 64 for B = 64.
+template <int BQ>
+constexpr int kTileKeys = BQ >= 128 ? 128 : 64;
+
+template <int D, int KT, int NWAVES>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t* lds, int wave,
                                           int lane) {
   constexpr int kChunksPerRow = D / 8;
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
-  constexpr int kInsts = kKT / kRowsPerInst;   // 1 KB instructions per tile
+  constexpr int kInsts = KT / kRowsPerInst;    // 1 KB instructions per tile
   static_assert(kInsts % NWAVES == 0, "tile instructions must split evenly over waves");
   // uniform tile base (scalar) + per-lane 32-bit byte offset: the load uses
   // the scalar-base addressing form, no 64-bit vector address math
@@ -116,6 +120,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
   constexpr int kBlockWaves = BQ / 32;          // waves per query block
   constexpr int kWaves = 2 * kBlockWaves;        // a workgroup covers two query blocks
   constexpr int kThreads = kWaves * 64;
+  constexpr int kKT = kTileKeys<BQ>;            // keys per LDS tile
   constexpr int kTilesPerBlock = BQ / kKT;
   constexpr int kTileBytes = kKT * D * 2;
   // Two K/V buffers as distinct objects: with the loop unrolled by two every
@@ -282,8 +287,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
   bool mine = false;
   int key0 = ntiles > 0 ? tile_info(0, mine) : -1;
   if (key0 >= 0) {
-    load_tile<D, kWaves>(Kg, key0, sK0, wave, lane);
-    load_tile<D, kWaves>(Vg, key0, sV0, wave, lane);
+    load_tile<D, kKT, kWaves>(Kg, key0, sK0, wave, lane);
+    load_tile<D, kKT, kWaves>(Vg, key0, sV0, wave, lane);
   }
   wait_vmem();
   __syncthreads();
@@ -295,42 +300,46 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     bool mine_next = false;
     const int key0_next = (n + 1 < ntiles) ? tile_info(n + 1, mine_next) : -1;
     if (key0_next >= 0) {
-      load_tile<D, kWaves>(Kg, key0_next, nK, wave, lane);
-      load_tile<D, kWaves>(Vg, key0_next, nV, wave, lane);
+      load_tile<D, kKT, kWaves>(Kg, key0_next, nK, wave, lane);
+      load_tile<D, kKT, kWaves>(Vg, key0_next, nV, wave, lane);
     }
     if (key0 >= 0 && mine && !(p.causal && key0 > qwave0 + 31)) {
-      // S^T (64 keys x 32 queries) as two 32x32 tiles.  K fragments are read
+      // S^T (kKT keys x 32 queries) as kNS 32x32 tiles.  K fragments are read
       // kAhead k-steps before their MFMAs so LDS latency overlaps the matrix
       // work instead of stalling each MFMA.
       constexpr int kSteps = D / 16;
-      constexpr int kAhead = 3;
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-      bf16x8_t kfr[kAhead + 1][2];
+      constexpr int kNS = kKT / 32;                // 32-key sub-tiles
+      constexpr int kNU = kKT / 16;                // 16-key chunks of P
+      constexpr int kAhead = kNS >= 4 ? 1 : 3;
+      f32x16_t s[kNS];
+#pragma unroll
+      for (int i = 0; i < kNS; ++i) s[i] = f32x16_t{};
+      bf16x8_t kfr[kAhead + 1][kNS];
 #pragma unroll
       for (int t = 0; t < kAhead; ++t)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kNS; ++i)
           kfr[t][i] = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
 #pragma unroll
       for (int t = 0; t < kSteps; ++t) {
         if (t + kAhead < kSteps) {
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < kNS; ++i)
             kfr[(t + kAhead) % (kAhead + 1)][i] =
                 as_bf16x8(*(const u32x4_t*)(sK + koff[t + kAhead] + i * 32 * D * 2));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) s[i] = mfma_32x32x16(kfr[t % (kAhead + 1)][i], qf[t], s[i]);
+        for (int i = 0; i < kNS; ++i) s[i] = mfma_32x32x16(kfr[t % (kAhead + 1)][i], qf[t], s[i]);
       }
       // Keep the reads kAhead steps ahead: the scheduler otherwise sinks them
       // next to their MFMAs.  (mask 0x100: DS read, 0x008: MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kNS * kAhead, 0);
 #pragma unroll
       for (int t = 0; t < kSteps - kAhead; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kNS, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kNS, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kAhead, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kNS * kAhead, 0);
       __builtin_amdgcn_sched_barrier(0);
       // V^T fragments (A operand of O^T += V^T P^T) of 16-key chunk u and
       // output column block dt, by transposed LDS reads; chunk 0 is read now
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < kNS; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int key = key0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       }
       float mloc = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kNS; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
       mloc = max_with_other_half(mloc) * p.scale_log2;
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
         m = mnew;
       }
       const float mref = (m == -INFINITY) ? 0.f : m;
-      // P in bf16 in four chunks of 16 keys; the denominator sums the same
+      // P in bf16 in chunks of 16 keys; the denominator sums the same
       // rounded values (packed dot2, in chunk order).  The MFMAs of chunk u
       // are interleaved with the exponentials and V reads of chunk u + 1
       // (fenced, so the vector and matrix work of one wave overlap).
@@ -398,18 +407,18 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       for (int e = 0; e < 4; ++e) pk[e] = p_pair(0, e);
       bf16x8_t pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kNU; ++u) {
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) {
           o[dt] = mfma_32x32x16(vf[u & 1][dt], pcur, o[dt]);
-          if (u < 3) {
+          if (u < kNU - 1) {
             vf[(u + 1) & 1][dt] = read_v(u + 1, dt);
 #pragma unroll
             for (int e = dt * kPairsPerDt; e < (dt + 1) * kPairsPerDt; ++e) pk[e] = p_pair(u + 1, e);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (u < 3) pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        if (u < kNU - 1) pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
       }
       lsum += rs0 + rs1;
     }
