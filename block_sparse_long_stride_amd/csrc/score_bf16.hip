@@ -23,6 +23,8 @@
 // Kernel 2 (score_fixup): per 32 reshaped rows, combines the range snapshots
 // into the row's softmax max and denominator, rescales the partial block sums,
 // adds the B/S rows of each query block and divides by B/S.
+// Kernel 2' (score_select_fused, xattn_score_select): kernel 2 with the
+// threshold selection of its query blocks' rows in the same workgroup.
 #include <algorithm>
 
 #include "common.h"
