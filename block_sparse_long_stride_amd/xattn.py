@@ -106,6 +106,22 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _device_buffer(t, name: str, shape, dtype, device) -> None:
+    """A caller-supplied buffer must be exactly what the kernels index: a
+    contiguous tensor of this shape and dtype on the inputs' device."""
+    if not (t.is_cuda and t.device == device and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+def _byte_buffer(t, name: str, device) -> int:
+    if not (t.is_cuda and t.device == device and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    return t.numel() * t.element_size()
+
+
 def shape_of(Q, K, causal: bool) -> Shape:
     torch = _torch()
     if Q.dim() != 3 or K.dim() != 3:
@@ -119,8 +135,8 @@ def shape_of(Q, K, causal: bool) -> Shape:
     if K.dtype != Q.dtype or Q.shape[1:] != K.shape[1:]:
         raise ValueError("Q and K must share dtype, L and d")
     for t in (Q, K):
-        if not (t.is_cuda and t.is_contiguous()):
-            raise ValueError("tensors must be contiguous device tensors")
+        if not (t.is_cuda and t.device == Q.device and t.is_contiguous()):
+            raise ValueError("Q and K must be contiguous tensors on one device")
     return Shape(Q.shape[0], K.shape[0], Q.shape[1], Q.shape[2], dt, int(bool(causal)))
 
 
@@ -139,10 +155,12 @@ def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None,
     NB = sh.L // B if B > 0 else 0
     if scores is None:
         scores = torch.empty((sh.hq, NB, NB), dtype=torch.float32, device=Q.device)
+    else:
+        _device_buffer(scores, "scores", (sh.hq, NB, NB), torch.float32, Q.device)
     need = xattn_score_workspace_bytes(sh, S, B)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else _byte_buffer(workspace, "workspace", Q.device)
     if phase is None:
         _check(lib().xattn_score(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B, _ptr(scores),
                                  _ptr(workspace), ws_bytes, _stream(stream)), "xattn_score")
@@ -160,37 +178,39 @@ def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None,
 def xattn_select(scores, tau: Sequence[float], causal: bool, mask=None, idx=None, counts=None,
                  stream=None) -> Tuple:
     """(mask uint64-as-int64 [hq][NB][words], idx int32 [hq][NB][NB], counts int32 [hq][NB])."""
-    torch = _torch()
-    import numpy as np
-    hq, NB = scores.shape[0], scores.shape[1]
-    if not (scores.is_cuda and scores.is_contiguous() and scores.dtype == torch.float32):
-        raise ValueError("scores must be a contiguous fp32 device tensor")
-    tau_np = np.ascontiguousarray(np.broadcast_to(np.asarray(tau, dtype=np.float32), (hq,)))
-    words = (NB + 63) // 64
-    if mask is None:
-        mask = torch.empty((hq, NB, words), dtype=torch.int64, device=scores.device)
-    if idx is None:
-        idx = torch.empty((hq, NB, NB), dtype=torch.int32, device=scores.device)
-    if counts is None:
-        counts = torch.empty((hq, NB), dtype=torch.int32, device=scores.device)
+    hq, NB, mask, idx, counts = _select_outputs(scores, mask, idx, counts)
+    tau_np = _tau_host(tau, hq)
     _check(lib().xattn_select(hq, NB, int(bool(causal)), _ptr(scores),
                               tau_np.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(idx),
                               _ptr(counts), _stream(stream)), "xattn_select")
     return mask, idx, counts
 
 
+def _mask_idx_counts(hq, NB, mask, idx, counts, device):
+    """Selection outputs: allocated when None, else checked against the
+    layout the kernels write."""
+    torch = _torch()
+    words = (NB + 63) // 64
+    outs = []
+    for t, name, shp, dt in ((mask, "mask", (hq, NB, words), torch.int64),
+                             (idx, "idx", (hq, NB, NB), torch.int32),
+                             (counts, "counts", (hq, NB), torch.int32)):
+        if t is None:
+            t = torch.empty(shp, dtype=dt, device=device)
+        else:
+            _device_buffer(t, name, shp, dt, device)
+        outs.append(t)
+    return outs
+
+
 def _select_outputs(scores, mask, idx, counts):
     torch = _torch()
+    if scores.dim() != 3 or scores.shape[1] != scores.shape[2]:
+        raise ValueError("scores must be [hq][NB][NB]")
     hq, NB = scores.shape[0], scores.shape[1]
     if not (scores.is_cuda and scores.is_contiguous() and scores.dtype == torch.float32):
         raise ValueError("scores must be a contiguous fp32 device tensor")
-    words = (NB + 63) // 64
-    if mask is None:
-        mask = torch.empty((hq, NB, words), dtype=torch.int64, device=scores.device)
-    if idx is None:
-        idx = torch.empty((hq, NB, NB), dtype=torch.int32, device=scores.device)
-    if counts is None:
-        counts = torch.empty((hq, NB), dtype=torch.int32, device=scores.device)
+    mask, idx, counts = _mask_idx_counts(hq, NB, mask, idx, counts, scores.device)
     return hq, NB, mask, idx, counts
 
 
@@ -225,21 +245,15 @@ def xattn_score_select(Q, K, S: int, B: int, tau: Sequence[float], causal: bool,
     torch = _torch()
     sh = shape_of(Q, K, causal)
     NB = sh.L // B if B > 0 else 0
-    words = (NB + 63) // 64
-    if mask is None:
-        mask = torch.empty((sh.hq, NB, words), dtype=torch.int64, device=Q.device)
-    if idx is None:
-        idx = torch.empty((sh.hq, NB, NB), dtype=torch.int32, device=Q.device)
-    if counts is None:
-        counts = torch.empty((sh.hq, NB), dtype=torch.int32, device=Q.device)
+    mask, idx, counts = _mask_idx_counts(sh.hq, NB, mask, idx, counts, Q.device)
     need = xattn_score_workspace_bytes(sh, S, B)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    ws_bytes = _byte_buffer(workspace, "workspace", Q.device)
     t = _tau_host(tau, sh.hq)
     _check(lib().xattn_score_select(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B,
                                     t.ctypes.data_as(ctypes.c_void_p), _ptr(mask), _ptr(idx),
-                                    _ptr(counts), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+                                    _ptr(counts), _ptr(workspace), ws_bytes, _stream(stream)),
            "xattn_score_select")
     return mask, idx, counts
 
@@ -254,14 +268,12 @@ def xattn_dit_attention(Q, K, V, S: int, B: int, tau: Sequence[float], step: int
     """One denoising step's attention under the full-attention warm-up policy."""
     torch = _torch()
     sh = shape_of(Q, K, causal)
-    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
-        raise ValueError("V must match K")
-    if out is None:
-        out = torch.empty_like(Q)
+    _check_v(V, K)
+    out = _attn_out(out, Q)
     if workspace is None and step >= warmup_steps:
         workspace = torch.empty(max(xattn_dit_workspace_bytes(sh, S, B), 1), dtype=torch.uint8,
                                 device=Q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else _byte_buffer(workspace, "workspace", Q.device)
     t = _tau_host(tau, sh.hq)
     _check(lib().xattn_dit_attention(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), S, B,
                                      t.ctypes.data_as(ctypes.c_void_p), int(step),
@@ -275,13 +287,16 @@ def xattn_head_error(O_sparse, O_dense, err=None, stream=None):
     torch = _torch()
     if O_sparse.shape != O_dense.shape or O_sparse.dtype != O_dense.dtype or O_sparse.dim() != 3:
         raise ValueError("O_sparse and O_dense must be [hq][L][d] tensors of one dtype")
-    if not (O_sparse.is_contiguous() and O_dense.is_contiguous()):
-        raise ValueError("outputs must be contiguous")
+    for t in (O_sparse, O_dense):
+        if not (t.is_cuda and t.device == O_dense.device and t.is_contiguous()):
+            raise ValueError("outputs must be contiguous tensors on one device")
     hq, L, d = O_dense.shape
     dt = XATTN_BF16 if O_dense.dtype == torch.bfloat16 else XATTN_FP32
     sh = Shape(hq, hq, L, d, dt, 0)
     if err is None:
         err = torch.empty(hq, dtype=torch.float64, device=O_dense.device)
+    else:
+        _device_buffer(err, "err", (hq,), torch.float64, O_dense.device)
     _check(lib().xattn_head_error(ctypes.byref(sh), _ptr(O_sparse), _ptr(O_dense), _ptr(err),
                                   _stream(stream)), "xattn_head_error")
     return err
@@ -302,13 +317,29 @@ def xattn_tau_dp(err, steps: int) -> Tuple[list, float]:
     return [int(x) for x in out], float(best.value)
 
 
+def _check_v(V, K) -> None:
+    if V.shape != K.shape or V.dtype != K.dtype or not (V.is_cuda and V.device == K.device
+                                                         and V.is_contiguous()):
+        raise ValueError("V must match K (shape, dtype, device) and be contiguous")
+
+
+def _attn_out(out, Q):
+    if out is None:
+        return _torch().empty_like(Q)
+    _device_buffer(out, "out", tuple(Q.shape), Q.dtype, Q.device)
+    return out
+
+
 def xattn_sparse_prefill(Q, K, V, B: int, idx, counts, causal: bool, out=None, stream=None):
     torch = _torch()
     sh = shape_of(Q, K, causal)
-    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
-        raise ValueError("V must match K")
-    if out is None:
-        out = torch.empty_like(Q)
+    _check_v(V, K)
+    if B < 1 or sh.L % B:
+        raise ValueError(f"L = {sh.L} must be a positive multiple of B = {B}")
+    NB = sh.L // B
+    _device_buffer(idx, "idx", (sh.hq, NB, NB), torch.int32, Q.device)
+    _device_buffer(counts, "counts", (sh.hq, NB), torch.int32, Q.device)
+    out = _attn_out(out, Q)
     _check(lib().xattn_sparse_prefill(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), B, _ptr(idx),
                                       _ptr(counts), _ptr(out), _stream(stream)),
            "xattn_sparse_prefill")
@@ -316,12 +347,9 @@ def xattn_sparse_prefill(Q, K, V, B: int, idx, counts, causal: bool, out=None, s
 
 
 def xattn_full(Q, K, V, causal: bool, out=None, stream=None):
-    torch = _torch()
     sh = shape_of(Q, K, causal)
-    if V.shape != K.shape or V.dtype != K.dtype or not V.is_contiguous():
-        raise ValueError("V must match K")
-    if out is None:
-        out = torch.empty_like(Q)
+    _check_v(V, K)
+    out = _attn_out(out, Q)
     _check(lib().xattn_full(ctypes.byref(sh), _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
                             _stream(stream)), "xattn_full")
     return out

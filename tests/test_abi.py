@@ -186,3 +186,23 @@ def test_status_strings():
     lib = X.lib()
     for s in range(5):
         assert lib.xattn_status_str(s)
+
+
+def test_binding_rejects_host_tensors_before_any_library_call():
+    """The Python layer hands the kernels device pointers only: host tensors
+    are refused before the library is called."""
+    import torch
+    Q = torch.zeros((2, 256, 64), dtype=torch.bfloat16)
+    K = torch.zeros((1, 256, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        X.xattn_score(Q, K, 8, 64, True)
+    with pytest.raises(ValueError):
+        X.xattn_select(torch.zeros((2, 4, 4), dtype=torch.float32), [0.9, 0.9], True)
+    with pytest.raises(ValueError):
+        X.xattn_select_topk(torch.zeros((2, 4, 4), dtype=torch.float32), 2, True)
+    with pytest.raises(ValueError):
+        X.xattn_sparse_prefill(Q, K, K, 64, None, None, True)
+    with pytest.raises(ValueError):
+        X.xattn_full(Q, K, K, True)
+    with pytest.raises(ValueError):
+        X.xattn_select(torch.zeros((2, 4, 5), dtype=torch.float32), [0.9, 0.9], True)
