@@ -310,7 +310,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       constexpr int kSteps = D / 16;
       constexpr int kNS = kKT / 32;                // 32-key sub-tiles
       constexpr int kNU = kKT / 16;                // 16-key chunks of P
-      constexpr int kAhead = kNS >= 4 ? 1 : 3;
+      constexpr int kAhead = kNS >= 4 ? 2 : 3;
       f32x16_t s[kNS];
 #pragma unroll
       for (int i = 0; i < kNS; ++i) s[i] = f32x16_t{};
@@ -356,13 +356,15 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       for (int dt = 0; dt < D / 32; ++dt) vf[0][dt] = read_v(0, dt);
       __builtin_amdgcn_sched_barrier(0);
       if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
+        // key = key0 + 4 hi + (32 i + 8 (v / 4) + v % 4) is masked when it
+        // exceeds qrow: one per-lane bound against compile-time offsets (no
+        // per-element key constants held in registers across the loop)
+        const int bound = qrow - key0 - 4 * hi;
 #pragma unroll
         for (int i = 0; i < kNS; ++i)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + 32 * i + 8 * (v >> 2) + 4 * hi + (v & 3);
-            if (key > qrow) s[i][v] = -INFINITY;
-          }
+          for (int v = 0; v < 16; ++v)
+            if (32 * i + 8 * (v >> 2) + (v & 3) > bound) s[i][v] = -INFINITY;
       }
       float mloc = -INFINITY;
 #pragma unroll
