@@ -451,15 +451,26 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     }
 }
 
+// dynamic LDS of the sparse mode: the merged block list, two bitmaps, offsets
+size_t list_bytes(int NB) {
+  const int nw32 = (NB + 31) / 32;
+  return (size_t)(NB + 3 * nw32 + 1) * sizeof(int32_t);
+}
+
 template <int D, int BQ>
 hipError_t launch(const FlashParams& fp, hipStream_t st) {
-  const int nw32 = (fp.NB + 31) / 32;
-  const size_t list_bytes = fp.idx ? (size_t)(fp.NB + 3 * nw32 + 1) * sizeof(int32_t) : 0;
-  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 4), list_bytes, st, fp);
+  const size_t dyn = fp.idx ? list_bytes(fp.NB) : 0;
+  hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 4), dyn, st, fp);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t flash_bf16_lds_bytes(int d, int B, int NB, bool sparse) {
+  const int keys = B >= 128 ? kTileKeys<128> : kTileKeys<64>;
+  const size_t tiles = (size_t)4 * keys * d * 2;   // K and V, two stages
+  return tiles + (sparse ? list_bytes(NB) : 0);
+}
 
 hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                              int B, const int32_t* idx, const int32_t* counts, void* O,

@@ -65,6 +65,10 @@ double tau_dp(int H, int R, const double* err, int steps, int* levels);
 
 // ---- attention ---------------------------------------------------------------
 // idx == nullptr selects dense mode (every key block, causal-limited).
+// LDS bytes one bf16 attention work-group needs (d in {64, 128}, B in {64, 128}).
+size_t flash_bf16_lds_bytes(int d, int B, int NB, bool sparse);
+constexpr size_t kLdsBytesPerCu = 160 * 1024;   // gfx950
+
 hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                              int B, const int32_t* idx, const int32_t* counts, void* O,
                              hipStream_t st);

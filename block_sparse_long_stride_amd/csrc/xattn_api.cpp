@@ -221,6 +221,17 @@ xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const
   if (st != XATTN_OK) return st;
   if (!Q || !K || !V || !O || !idx || !counts)
     return fail(XATTN_EINVAL, "Q, K, V, O, idx and counts must be non-NULL");
+  if (s.bf16) {
+    // the work-group keeps its two query blocks' merged block list in LDS
+    // beside the K/V tiles
+    const int NB = s.L / B;
+    const size_t need = xattn::flash_bf16_lds_bytes(s.d, B, NB, true);
+    if (need > xattn::kLdsBytesPerCu)
+      return fail(XATTN_EUNSUPPORTED,
+                  "bf16 sparse prefill needs %zu bytes of LDS for NB = %d (B = %d, d = %d); "
+                  "the limit is %zu",
+                  need, NB, B, s.d, xattn::kLdsBytesPerCu);
+  }
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = s.bf16 ? xattn::launch_flash_bf16(s, Q, K, V, B, idx, counts, O, hs)
                         : xattn::launch_flash_fp32(s, Q, K, V, B, idx, counts, O, hs);

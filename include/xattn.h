@@ -227,8 +227,10 @@ xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, in
  *                entry counts once and blocks are visited in ascending
  *                order.  A row with no key gets O = 0.
  *   O            out, [hq][L][d] in the input dtype, fully overwritten.
- * Requires L % B == 0.  bf16 kernels cover d in {64, 128}, B in {64, 128};
- * fp32 kernels cover d <= 128, B <= 256.
+ * Requires L % B == 0.  bf16 kernels cover d in {64, 128}, B in {64, 128},
+ * and NB up to what fits in one CU's LDS beside the K/V tiles (B = 128,
+ * d = 128: NB <= 7488, i.e. L <= 958464; more: XATTN_EUNSUPPORTED); fp32
+ * kernels cover d <= 128, B <= 256.
  */
 xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
                                   const void* V, int32_t B, const int32_t* idx,

@@ -175,6 +175,12 @@ def test_attention_rejects():
                                     None) == X.XATTN_EINVAL
     assert lib.xattn_sparse_prefill(ctypes.byref(sh), DUMMY, DUMMY, DUMMY, 128, None, DUMMY, DUMMY,
                                     None) == X.XATTN_EINVAL
+    # bf16, B = 128, d = 128: the merged block list of NB = 7489 blocks no
+    # longer fits in LDS beside the K/V tiles (7488 does)
+    big = _shape(hq=1, hkv=1, L=7489 * 128)
+    assert lib.xattn_sparse_prefill(ctypes.byref(big), DUMMY, DUMMY, DUMMY, 128, DUMMY, DUMMY,
+                                    DUMMY, None) == X.XATTN_EUNSUPPORTED
+    assert b"LDS" in lib.xattn_last_error()
     assert lib.xattn_full(ctypes.byref(_shape(L=4000)), DUMMY, DUMMY, DUMMY, DUMMY,
                           None) == X.XATTN_EUNSUPPORTED
     assert lib.xattn_full(ctypes.byref(_shape(d=80)), DUMMY, DUMMY, DUMMY, DUMMY,
