@@ -69,6 +69,10 @@ xattn_status check_score_args(const xattn_shape* shape, int S, int B, xattn::Sha
       return fail(XATTN_EUNSUPPORTED, "bf16 scoring covers d in {64, 128}, got %d", s->d);
     if (bs != 4 && bs != 8 && bs != 16 && bs != 32)
       return fail(XATTN_EUNSUPPORTED, "bf16 scoring covers B/S in {4, 8, 16, 32}, got %d", bs);
+    // one head's Q or K is addressed through a buffer resource of 32-bit size
+    if ((long long)s->L * s->d * 2 > 0x7FFFFFFFll)
+      return fail(XATTN_EUNSUPPORTED, "bf16 scoring covers L * d * 2 < 2^31 bytes per head, got L=%d d=%d",
+                  s->L, s->d);
   } else {
     if (s->d > 1024) return fail(XATTN_EUNSUPPORTED, "fp32 scoring covers d <= 1024");
     if (bs > 256) return fail(XATTN_EUNSUPPORTED, "fp32 scoring covers B/S <= 256");

@@ -83,8 +83,9 @@ size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t 
  *              entries kb > qb are 0 when causal.
  *   workspace  device scratch of at least xattn_score_workspace_bytes().
  * Requires L % B == 0 and B % S == 0 (else XATTN_EINVAL).  bf16 kernels
- * cover d in {64, 128} and B/S in {4, 8, 16, 32}; fp32 kernels cover d <= 128
- * (else XATTN_EUNSUPPORTED).
+ * cover d in {64, 128}, B/S in {4, 8, 16, 32} and L * d * 2 < 2^31 bytes per
+ * head; fp32 kernels cover d <= 1024 and B/S <= 256 (else
+ * XATTN_EUNSUPPORTED).
  */
 xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
                          int32_t S, int32_t B, float* scores, void* workspace,

@@ -62,6 +62,14 @@ def test_score_rejects(kw, S, B, status):
     assert X.lib().xattn_last_error()
 
 
+def test_score_rejects_heads_beyond_32_bit_buffers():
+    lib = X.lib()
+    sh = _shape(hq=1, hkv=1, L=1 << 23, d=128)   # 2^31 bytes per head
+    assert lib.xattn_score(ctypes.byref(sh), DUMMY, DUMMY, 16, 128, DUMMY, DUMMY, 1 << 40,
+                           None) == X.XATTN_EUNSUPPORTED
+    assert b"2^31" in lib.xattn_last_error()
+
+
 def test_score_workspace_checks():
     lib = X.lib()
     sh = _shape()
