@@ -73,6 +73,11 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 template <int BQ>
 constexpr int kTileKeys = BQ >= 128 ? 128 : 64;
 
+// Query-block pairs per scheduling chunk (times the heads of a KV group).
+// Small chunks keep the work per XCD even; with the alternating deal below,
+// two and four pairs measure the same, one pair and eight or more are slower.
+constexpr int kPairsPerChunk = 2;
+
 template <int D, int KT, int NWAVES>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t* lds, int wave,
                                           int lane) {
@@ -134,13 +139,16 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
 
   // Work order.  A work item is a pair of neighbouring query blocks (2i,
   // 2i+1) of one head.  Items of one KV group are (pair descending, head),
-  // cut into chunks of 4 pairs x all heads of the group.  Chunks are dealt
-  // round-robin to the 8 XCDs and every XCD runs through the groups in the
-  // same order, so (a) all XCDs work on the same KV group at a time -- its
-  // K/V stays resident in the memory-side cache -- and (b) the work-groups on
-  // one XCD share neighbouring query blocks and all heads of the group in its
-  // L2.  When the counts do not divide evenly, each XCD takes a contiguous
-  // range instead (one KV group per XCD).
+  // cut into chunks of kPairsPerChunk pairs x all heads of the group.
+  // Chunks are dealt to the 8 XCDs in rounds of eight, the XCD order
+  // reversed every other round, and every XCD runs through the groups in
+  // the same order, so (a) all XCDs work on the same KV group at a time --
+  // its K/V stays resident in the memory-side cache -- (b) the work-groups
+  // on one XCD run all heads of the group on the same query blocks, and (c)
+  // the XCDs get equal work: causal pairs shrink along the order, and a
+  // plain round-robin deal would give XCD 0 the longest pair of every
+  // round.  When the counts do not divide evenly, each XCD takes a
+  // contiguous range instead (one KV group per XCD).
   const int npairs = (p.NB + 1) / 2;
   const int per_group = npairs * p.group;
   int g, rem;
@@ -148,10 +156,11 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     const int bid = blockIdx.x;
     const int xcd = bid % kNumXcd, k = bid / kNumXcd;
     const int per_xcd = per_group / kNumXcd;     // items of one group on one XCD
-    const int chunk = 4 * p.group;               // items per chunk
+    const int chunk = kPairsPerChunk * p.group;  // items per chunk
     g = k / per_xcd;
     const int kk = k % per_xcd;
-    rem = ((kk / chunk) * kNumXcd + xcd) * chunk + kk % chunk;
+    const int r = kk / chunk;                    // round
+    rem = (r * kNumXcd + ((r & 1) ? kNumXcd - 1 - xcd : xcd)) * chunk + kk % chunk;
     if (g >= p.hq / p.group) return;
   } else {
     const int w = xcd_swizzle(blockIdx.x, p.grid);
@@ -490,7 +499,7 @@ hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const
   const int npairs = (fp.NB + 1) / 2;
   fp.nwork = npairs * s.hq;
   fp.grid = (fp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
-  fp.interleave = (npairs * fp.group) % (kNumXcd * 4 * fp.group) == 0;
+  fp.interleave = (npairs * fp.group) % (kNumXcd * kPairsPerChunk * fp.group) == 0;
   fp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
   if (s.d == 128) return B == 128 ? launch<128, 128>(fp, st) : launch<128, 64>(fp, st);
   return B == 128 ? launch<64, 128>(fp, st) : launch<64, 64>(fp, st);
