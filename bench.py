@@ -41,7 +41,9 @@ def parse():
     ap.add_argument("--no-full", action="store_true", help="skip timing xattn_full")
     ap.add_argument("--cpu-sample-seconds", type=float, default=20.0)
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the measurements of the NEXT rows (selection cut rules ...)")
+                    help="skip the measurements beside the headline step (Top-K / Top-Ratio "
+                         "selection, sampling patterns, fused scoring + selection, tau "
+                         "calibration, DiT warm-up policy)")
     ap.add_argument("--no-dit", dest="next_dit", action="store_false",
                     help="skip the video-DiT warm-up policy measurement (config 5)")
     ap.add_argument("--only", choices=["score", "select", "sparse", "full", "copy"],
@@ -270,8 +272,8 @@ def main():
         torch.cuda.synchronize()
         full_ms = ef[0].elapsed_time(ef[1])
 
-    # NEXT rows measured beside the headline (not part of the timed step)
-    next_rows = {}
+    # variants measured beside the headline (not part of the timed step)
+    variants = {}
     if not args.no_next:
         def timed(fn, reps=5):
             e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -292,7 +294,7 @@ def main():
             ms_r = timed(fn)
             n_r = int(counts.to(torch.int64).sum())
             b_r = 4.0 * valid + mask.numel() * 8 + 4.0 * hq * NB * NB + 4.0 * hq * NB
-            next_rows["f1_" + name] = {
+            variants[name] = {
                 "param": f"K={kblk * cfg.B} tokens ({kblk} blocks)" if name == "select_topk"
                          else "ratio=0.27",
                 "ms": round(ms_r, 3), "gbs": round(b_r / (ms_r * 1e-3) / 1e9, 1),
@@ -308,7 +310,7 @@ def main():
                                stream=stream)
             torch.cuda.synchronize()
             n_p = int(counts.to(torch.int64).sum())
-            next_rows["f3_score_" + name] = {
+            variants["score_" + name] = {
                 "phase": ph, "ms": round(ms_p, 3),
                 "tflops": round(F_score / (ms_p * 1e-3) / 1e12, 1),
                 "frac_bf16_peak": round(F_score / (ms_p * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -319,7 +321,7 @@ def main():
             ms_f = timed(lambda: xattn.xattn_score_select(Q, K, cfg.S, cfg.B, w.tau, cfg.causal,
                                                           mask=mask, idx=idx, counts=counts,
                                                           workspace=ws, stream=stream))
-            next_rows["f2_score_select_fused"] = {
+            variants["score_select_fused"] = {
                 "ms": round(ms_f, 3), "two_calls_ms": round(score_ms + select_ms, 3),
                 "density": round(int(counts.to(torch.int64).sum()) / valid, 5)}
         # per-head threshold calibration: tau0 * 0.9^k (k = 0 .. 2) for every head,
@@ -349,7 +351,7 @@ def main():
                                stream=stream)
             torch.cuda.synchronize()
             d_cal = int(counts.to(torch.int64).sum()) / valid
-            next_rows["f4_tau_dp"] = {
+            variants["tau_calibration"] = {
                 "tau0": t0c, "levels": R_lv, "steps": hq, "calibration_ms": round(calib_ms, 1),
                 "mean_tau": round(float(np.mean(tau_h)), 4),
                 "heads_per_level": [levels.count(k) for k in range(R_lv + 1)],
@@ -358,7 +360,7 @@ def main():
             del dense, spo
         # video-DiT warm-up policy on the config-5 workload (non-causal video tokens)
         if args.next_dit:
-            next_rows["f2_dit_policy"] = dit_policy_rows(timed, stream)
+            variants["dit_warmup_policy"] = dit_policy_rows(timed, stream)
         # restore the threshold selection for anything that follows
         xattn.xattn_select(scores, w.tau, cfg.causal, mask=mask, idx=idx, counts=counts,
                            stream=stream)
@@ -408,7 +410,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("flash_bf16", f"config{cfg.cid}")},
         "cpu_baseline": None,
-        "next_rows": next_rows or None,
+        "variants": variants or None,
     }
     if not args.no_cpu_baseline:
         ms_cpu, rows, threads = cpu_baseline(cfg, w, args.cpu_sample_seconds)
