@@ -30,6 +30,11 @@ SMALL = {
     # and L/S = 528, a ragged last scoring tile
     "llm-odd-blocks": get_config(2, hq=2, hkv=1, L=4224),
     "noncausal-llm-fp32": get_config(1, causal=False, L=1024),
+    # the attention kernel's interleaved XCD work order (pairs of query blocks
+    # a multiple of 16), two rounds of chunks per XCD so the alternating deal
+    # is used, with one and with eight query heads per KV head
+    "llm-mha-interleave": get_config(2, hq=2, hkv=2, L=8192),
+    "llm-gqa8-interleave": get_config(3, hq=8, hkv=1, L=8192),
 }
 
 
