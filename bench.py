@@ -75,6 +75,18 @@ def measured_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, w, seconds):
     """Time the oracle (score rows, find_blocks, block-sparse attention) on a
     random sample of (head, query block) rows until `seconds` have elapsed,
@@ -416,7 +428,7 @@ def main():
         ms_cpu, rows, threads = cpu_baseline(cfg, w, args.cpu_sample_seconds)
         res["cpu_baseline"] = {"value": round(F_full / (ms_cpu * 1e-3) / 1e12, 6),
                                "unit": "TFLOP/s (dense-equivalent)", "cores": threads,
-                               "kind": "oracle", "ms_per_step": round(ms_cpu, 1),
+                               "cpu_model": cpu_model(), "kind": "oracle", "ms_per_step": round(ms_cpu, 1),
                                "sample": f"{rows} random (head, query block) rows of the same "
                                          f"workload through oracle score, find_blocks and "
                                          f"block-sparse attention (fp64 numpy), scaled to "

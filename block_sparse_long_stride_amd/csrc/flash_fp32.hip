@@ -113,6 +113,10 @@ hipError_t launch(const Fp32FlashParams& fp, int hq, hipStream_t st) {
 
 }  // namespace
 
+size_t flash_fp32_lds_bytes(int d, int NB, bool sparse) {
+  return (size_t)2 * kKT * d * sizeof(float) + (sparse ? (size_t)((NB + 31) / 32) * sizeof(uint32_t) : 0);
+}
+
 hipError_t launch_flash_fp32(const Shape& s, const void* Q, const void* K, const void* V,
                              int B, const int32_t* idx, const int32_t* counts, void* O,
                              hipStream_t st) {

@@ -72,6 +72,9 @@ constexpr size_t kLdsBytesPerCu = 160 * 1024;   // gfx950
 hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const void* V,
                              int B, const int32_t* idx, const int32_t* counts, void* O,
                              hipStream_t st);
+// LDS bytes one fp32 attention work-group needs (key/value tiles, and the
+// block bitmap in sparse mode).
+size_t flash_fp32_lds_bytes(int d, int NB, bool sparse);
 hipError_t launch_flash_fp32(const Shape& s, const void* Q, const void* K, const void* V,
                              int B, const int32_t* idx, const int32_t* counts, void* O,
                              hipStream_t st);

@@ -26,6 +26,7 @@
 // Kernel 2' (score_select_fused, xattn_score_select): kernel 2 with the
 // threshold selection of its query blocks' rows in the same workgroup.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "launch.h"
@@ -661,18 +662,21 @@ hipError_t launch_gemm_bs(const GemmParams& gp, int bs, hipStream_t st) {
 }
 
 // Compute units per XCD of the current device (the persistent GEMM runs one
-// workgroup per CU).
+// workgroup per CU).  Cached per device; several host threads may fill an
+// entry at once, all with the same value, so relaxed atomics suffice.
 int cus_per_xcd() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
-  if (cached[dev] == 0) {
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kNumXcd)
       n = 256;
-    cached[dev] = n / kNumXcd;
+    v = n / kNumXcd;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 struct WsLayout {

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <string>
 
 #include "../../include/xattn.h"
@@ -34,6 +35,16 @@ xattn_status ok() {
 xattn_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(XATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Every device buffer is read or written with 16-byte vector loads or
+// direct-to-LDS copies, so each must start on a 16-byte boundary (a tensor
+// view with an odd storage offset would otherwise reach the kernels).
+xattn_status check_aligned(std::initializer_list<const void*> ptrs, const char* names) {
+  for (const void* p : ptrs)
+    if ((uintptr_t)p % 16)
+      return fail(XATTN_EINVAL, "device buffers (%s) must be 16-byte aligned; got %p", names, p);
+  return XATTN_OK;
 }
 
 xattn_status check_shape(const xattn_shape* s, xattn::Shape* out) {
@@ -118,6 +129,8 @@ static xattn_status run_score(const xattn_shape* shape, const void* Q, const voi
   xattn_status st = check_score_args(shape, S, B, &s);
   if (st != XATTN_OK) return st;
   if (!Q || !K || !scores) return fail(XATTN_EINVAL, "Q, K and scores must be non-NULL");
+  st = check_aligned({Q, K, scores, workspace}, "Q, K, scores, workspace");
+  if (st != XATTN_OK) return st;
   const size_t need = xattn::score_workspace_bytes(s, S, B);
   if (need && !workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need)
@@ -168,6 +181,8 @@ xattn_status xattn_select(int32_t hq, int32_t NB, int32_t causal, const float* s
     return fail(XATTN_EUNSUPPORTED, "selection covers hq <= %d, got %d", xattn::kMaxHeads, hq);
   if (NB > xattn::kMaxSelectBlocks)
     return fail(XATTN_EUNSUPPORTED, "selection covers NB <= %d, got %d", xattn::kMaxSelectBlocks, NB);
+  xattn_status st = check_aligned({scores, mask, idx, counts}, "scores, mask, idx, counts");
+  if (st != XATTN_OK) return st;
   xattn::TauArray tau;
   for (int h = 0; h < xattn::kMaxHeads; ++h) tau.v[h] = 1.0f;
   for (int h = 0; h < hq; ++h) {
@@ -189,7 +204,7 @@ static xattn_status check_select_args(int32_t hq, int32_t NB, int32_t causal, co
     return fail(XATTN_EINVAL, "scores, mask, idx and counts must be non-NULL");
   if (NB > xattn::kMaxSelectBlocks)
     return fail(XATTN_EUNSUPPORTED, "selection covers NB <= %d, got %d", xattn::kMaxSelectBlocks, NB);
-  return XATTN_OK;
+  return check_aligned({scores, mask, idx, counts}, "scores, mask, idx, counts");
 }
 
 xattn_status xattn_select_topk(int32_t hq, int32_t NB, int32_t causal, const float* scores,
@@ -225,16 +240,19 @@ xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const
   if (st != XATTN_OK) return st;
   if (!Q || !K || !V || !O || !idx || !counts)
     return fail(XATTN_EINVAL, "Q, K, V, O, idx and counts must be non-NULL");
-  if (s.bf16) {
-    // the work-group keeps its two query blocks' merged block list in LDS
-    // beside the K/V tiles
+  st = check_aligned({Q, K, V, O, idx, counts}, "Q, K, V, O, idx, counts");
+  if (st != XATTN_OK) return st;
+  {
+    // the work-group keeps its query blocks' block list (bf16: two lists
+    // merged; fp32: a bitmap) in LDS beside the K/V tiles
     const int NB = s.L / B;
-    const size_t need = xattn::flash_bf16_lds_bytes(s.d, B, NB, true);
+    const size_t need = s.bf16 ? xattn::flash_bf16_lds_bytes(s.d, B, NB, true)
+                               : xattn::flash_fp32_lds_bytes(s.d, NB, true);
     if (need > xattn::kLdsBytesPerCu)
       return fail(XATTN_EUNSUPPORTED,
-                  "bf16 sparse prefill needs %zu bytes of LDS for NB = %d (B = %d, d = %d); "
+                  "%s sparse prefill needs %zu bytes of LDS for NB = %d (B = %d, d = %d); "
                   "the limit is %zu",
-                  need, NB, B, s.d, xattn::kLdsBytesPerCu);
+                  s.bf16 ? "bf16" : "fp32", need, NB, B, s.d, xattn::kLdsBytesPerCu);
   }
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e = s.bf16 ? xattn::launch_flash_bf16(s, Q, K, V, B, idx, counts, O, hs)
@@ -248,6 +266,8 @@ xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K, 
   xattn_status st = check_shape(shape, &s);
   if (st != XATTN_OK) return st;
   if (!Q || !K || !V || !O) return fail(XATTN_EINVAL, "Q, K, V and O must be non-NULL");
+  st = check_aligned({Q, K, V, O}, "Q, K, V, O");
+  if (st != XATTN_OK) return st;
   int B = 0;
   if (s.bf16) {
     B = (s.L % 128 == 0) ? 128 : (s.L % 64 == 0 ? 64 : 0);
@@ -306,6 +326,8 @@ xattn_status xattn_score_select(const xattn_shape* shape, const void* Q, const v
   if (st != XATTN_OK) return st;
   if (!Q || !K || !mask || !idx || !counts)
     return fail(XATTN_EINVAL, "Q, K, mask, idx and counts must be non-NULL");
+  st = check_aligned({Q, K, mask, idx, counts, workspace}, "Q, K, mask, idx, counts, workspace");
+  if (st != XATTN_OK) return st;
   const size_t need = xattn::score_workspace_bytes(s, S, B);
   if (!workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", need);
   if (workspace_bytes < need)
@@ -357,6 +379,8 @@ xattn_status xattn_dit_attention(const xattn_shape* shape, const void* Q, const 
   st = check_attn_args(s, B);
   if (st != XATTN_OK) return st;
   if (!Q || !K || !V || !O) return fail(XATTN_EINVAL, "Q, K, V and O must be non-NULL");
+  st = check_aligned({Q, K, V, O, workspace}, "Q, K, V, O, workspace");
+  if (st != XATTN_OK) return st;
   const DitLayout d = dit_layout(s, S, B);
   if (!workspace) return fail(XATTN_EINVAL, "workspace is NULL (%zu bytes needed)", d.total);
   if (workspace_bytes < d.total)

@@ -22,8 +22,11 @@
  *
  * Conventions for every call:
  *   - Batch 1.  Q and O are [hq][L][d], K and V are [hkv][L][d], contiguous
- *     row-major, dtype = shape->dtype (bf16 or fp32), 16-byte aligned device
- *     memory.  Query head h reads key/value head h / (hq / hkv).
+ *     row-major, dtype = shape->dtype (bf16 or fp32), device memory.  Query
+ *     head h reads key/value head h / (hq / hkv).
+ *   - Every device buffer (Q, K, V, O, scores, mask, idx, counts, err,
+ *     workspace) must start on a 16-byte boundary; a misaligned pointer is
+ *     refused with XATTN_EINVAL before any HIP call.
  *   - Every pointer except `tau_host` and `shape` is device memory owned by
  *     the caller.  The library allocates nothing, frees nothing and keeps no
  *     pointer after a call returns.
@@ -33,8 +36,10 @@
  *     error has enqueued nothing, except XATTN_EHIP (a launch failed).
  *     xattn_last_error() returns a thread-local description of the last
  *     error.  No C++ exception crosses this interface.
- *   - Calls keep no global state and are safe to issue from several host
- *     threads; calls on one stream run in order.
+ *   - Calls keep no mutable global state apart from a per-device cache of
+ *     the compute-unit count (filled once, atomically) and the thread-local
+ *     error string, and are safe to issue from several host threads; calls
+ *     on one stream run in order.
  */
 #ifndef XATTN_H
 #define XATTN_H
@@ -231,7 +236,8 @@ xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, in
  * Requires L % B == 0.  bf16 kernels cover d in {64, 128}, B in {64, 128},
  * and NB up to what fits in one CU's LDS beside the K/V tiles (B = 128,
  * d = 128: NB <= 7488, i.e. L <= 958464; more: XATTN_EUNSUPPORTED); fp32
- * kernels cover d <= 128, B <= 256.
+ * kernels cover d in {32, 64, 128}, B <= 256, and NB whose block bitmap fits
+ * in LDS beside the fp32 tiles (else XATTN_EUNSUPPORTED).
  */
 xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
                                   const void* V, int32_t B, const int32_t* idx,
@@ -239,8 +245,17 @@ xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const
 
 /*
  * Dense attention softmax(Q K^T / sqrt(d)) V (causal if shape->causal): the
- * exact attention the sparse path is measured against.  bf16 kernels need
- * L % 64 == 0 and d in {64, 128}; fp32 kernels cover d <= 128.
+ * exact attention the sparse path is measured against.  The pages' speed
+ * baseline is dense FlashAttention (papercache.org summary, section A4
+ * "baseline models": FlashAttention run through FlashInfer; chapterpal.com
+ * Knowl 6, "Prefill Acceleration and End-to-End Speedup", quotes the
+ * attention speedup against it); this call is that baseline on the same
+ * hardware, sharing the tiles and softmax of xattn_sparse_prefill with every
+ * causal-visible key block visited.
+ *
+ *   O  out, [hq][L][d] in the input dtype, fully overwritten.
+ * bf16 kernels need L % 64 == 0 and d in {64, 128}; fp32 kernels cover
+ * d in {32, 64, 128} (else XATTN_EUNSUPPORTED).
  */
 xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K,
                         const void* V, void* O, void* stream);

@@ -220,3 +220,49 @@ def test_binding_rejects_host_tensors_before_any_library_call():
         X.xattn_full(Q, K, K, True)
     with pytest.raises(ValueError):
         X.xattn_select(torch.zeros((2, 4, 5), dtype=torch.float32), [0.9, 0.9], True)
+
+
+MIS = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+
+
+def test_every_entry_point_rejects_misaligned_device_buffers():
+    """The kernels read and write through 16-byte vector and direct-to-LDS
+    accesses: a device pointer off a 16-byte boundary is refused up front."""
+    lib = X.lib()
+    sh = _shape()
+    tau = (ctypes.c_float * 4)(0.9, 0.9, 0.9, 0.9)
+    phase = (ctypes.c_int32 * 16)(*range(16))
+    E = X.XATTN_EINVAL
+    for i in range(4):
+        a = [MIS if j == i else DUMMY for j in range(4)]
+        assert lib.xattn_score(ctypes.byref(sh), a[0], a[1], 16, 128, a[2], a[3], 1 << 40, None) == E
+        assert b"16-byte" in lib.xattn_last_error()
+        assert lib.xattn_score_pattern(ctypes.byref(sh), a[0], a[1], 16, 128, phase, a[2], a[3],
+                                       1 << 40, None) == E
+        assert lib.xattn_select(4, 32, 1, a[0], tau, a[1], a[2], a[3], None) == E
+        assert lib.xattn_select_topk(4, 32, 1, a[0], 2, a[1], a[2], a[3], None) == E
+        assert lib.xattn_select_topratio(4, 32, 1, a[0], 0.27, a[1], a[2], a[3], None) == E
+        assert lib.xattn_full(ctypes.byref(sh), a[0], a[1], a[2], a[3], None) == E
+    for i in range(6):
+        a = [MIS if j == i else DUMMY for j in range(6)]
+        assert lib.xattn_sparse_prefill(ctypes.byref(sh), a[0], a[1], a[2], 128, a[4], a[5], a[3],
+                                        None) == E
+        assert lib.xattn_score_select(ctypes.byref(sh), a[0], a[1], 16, 128, tau, a[2], a[3], a[4],
+                                      a[5], 1 << 40, None) == E
+    for i in range(5):
+        a = [MIS if j == i else DUMMY for j in range(5)]
+        assert lib.xattn_dit_attention(ctypes.byref(sh), a[0], a[1], a[2], 16, 128, tau, 7, 5, a[3],
+                                       a[4], 1 << 40, None) == E
+    assert lib.xattn_head_error(ctypes.byref(sh), MIS, DUMMY, DUMMY, None) == E
+
+
+def test_fp32_sparse_prefill_bounds_its_lds_bitmap():
+    """fp32 sparse prefill keeps a bitmap of NB bits beside its key/value
+    tiles: a block count whose bitmap no longer fits in one CU's LDS is
+    refused before any launch."""
+    lib = X.lib()
+    big = _shape(hq=1, hkv=1, L=1 << 21, d=128, dtype=X.XATTN_FP32)
+    # B = 1: NB = 2^21 blocks, a 256 KB bitmap beside 32 KB of tiles: too much
+    assert lib.xattn_sparse_prefill(ctypes.byref(big), DUMMY, DUMMY, DUMMY, 1, DUMMY, DUMMY, DUMMY,
+                                    None) == X.XATTN_EUNSUPPORTED
+    assert b"LDS" in lib.xattn_last_error()

@@ -60,3 +60,9 @@ def test_multi_gpu_request_is_refused():
     assert r.returncode == 2
     assert "--gpus must be 1" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_cpu_model_read_from_proc_cpuinfo():
+    m = bench.cpu_model()
+    if os.path.exists("/proc/cpuinfo"):
+        assert isinstance(m, str) and m

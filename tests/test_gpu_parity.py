@@ -177,8 +177,7 @@ def test_pipeline_masks_match_oracle(name):
             taus.append(float(w.tau[h]))
             labs.append(f"h{h} qb{qb}")
     rep = classify_rows(sels, srts, gsets, taus, labs)
-    print(f"[{name}] rows {rep.rows} equal {rep.equal} tau-band {rep.tau_band} "
-          f"tie-band {rep.tie_band} density "
+    print(f"[{name}] {rep.summary()} density "
           f"{sum(len(g) for g in gsets) / sum(s.n_valid for s in sels):.4f}")
     assert not rep.failures, rep.failures[:5]
 

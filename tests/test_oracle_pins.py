@@ -537,3 +537,21 @@ def test_head_rel_sq_error_properties():
     assert math.isclose(O.head_rel_sq_error(3 * a, 3 * b), O.head_rel_sq_error(a, b), rel_tol=1e-12)
     manual = sum(((a - b) ** 2).flat) / sum((b ** 2).flat)
     assert math.isclose(O.head_rel_sq_error(a, b), manual, rel_tol=1e-12)
+
+
+def test_to_mask_multi_word_layout():
+    """Mask words for NB > 64 (bit kb % 64 of word kb // 64), with the words
+    written out by hand: blocks {0, 63} -> word 0, {64, 65, 127} -> word 1,
+    {128} -> word 2, {199} -> word 3 (bit 7)."""
+    sel = O.Selection(selected=np.array([0, 63, 64, 65, 127, 128, 199]), kstar=7,
+                      order=np.array([0, 63, 64, 65, 127, 128, 199]), csum=np.ones(7), n_valid=200)
+    words = O.to_mask(sel, 200)
+    assert words.dtype == np.uint64 and words.shape == (4,)
+    assert [int(x) for x in words] == [0x8000000000000001, 0x8000000000000003, 0x1, 0x80]
+    # and against one big integer holding bit kb for every selected block
+    big = sum(1 << int(kb) for kb in sel.selected)
+    assert [int(x) for x in words] == [(big >> (64 * i)) & (2 ** 64 - 1) for i in range(4)]
+    # NB = 65: two words, the second holding only block 64
+    sel65 = O.find_blocks(np.r_[np.zeros(64), 1.0], 65, 0.5)
+    assert list(sel65.selected) == [64]
+    assert [int(x) for x in O.to_mask(sel65, 65)] == [0, 1]
