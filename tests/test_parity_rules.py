@@ -1,9 +1,9 @@
 """The mask comparison rule of the GPU parity tests, checked on the CPU with
-hand-built rows: outside the tau band only identical selections pass; inside
-it the cut may move by one block, but only along the oracle's ranking; a
-near-tie at the cut earns no exemption (find_blocks of the papercache.org
-summary, section 2.2: the shortest prefix of the ranking whose mass is >=
-tau)."""
+hand-built rows: outside the tau band only identical selections pass, a
+near-tie at the cut included; inside it the cut may move by one block and
+near-tied blocks may swap, but the set must stay a top set of the oracle's
+ranking (find_blocks of the papercache.org summary, section 2.2: the
+shortest prefix of the ranking whose mass is >= tau)."""
 import numpy as np
 
 import oracle as O
@@ -59,3 +59,18 @@ def test_near_tie_at_the_cut_is_not_exempt():
     rep = _classify(scores, 0.2, [1])
     assert len(rep.failures) == 1 and rep.tie_band == 1
     assert "tie band True" in rep.failures[0]
+
+
+def test_tau_band_accepts_a_near_tie_swap_but_not_a_real_one():
+    # blocks 1 and 2 differ by 1e-6 relative; tau sits 5e-5 above P_1
+    scores = np.array([0.5, 0.2, 0.2 * (1 - 1e-6), 0.1 + 0.2e-6])
+    tau = 0.5 + 5e-5
+    sel, srt = _row(scores, tau)
+    assert sel.kstar == 2 and list(sel.selected) == [0, 1]
+    assert in_tau_band(sel, tau) and in_tie_band(srt, sel)
+    rep = _classify(scores, tau, [0, 2])          # near-tied swap at the cut
+    assert not rep.failures and rep.tau_band_moved == 1
+    rep = _classify(scores, tau, [0, 3])          # block 3 is no near-tie of 1
+    assert len(rep.failures) == 1
+    rep = _classify(scores, tau, [1, 2])          # drops the top block
+    assert len(rep.failures) == 1
