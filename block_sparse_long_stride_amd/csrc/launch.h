@@ -27,6 +27,11 @@ struct PhaseMap {
   int32_t v[kMaxPhase];
 };
 size_t score_workspace_bytes(const Shape& s, int S, int B);
+// Fixed scratch of the allocation-free scoring entry point (a static device
+// array in score_bf16.hip): its size, and this device's address of it
+// (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kScoreScratchBytes = (size_t)64 << 20;
+hipError_t score_scratch_ptr(void** out);
 hipError_t launch_score_bf16(const Shape& s, const void* Q, const void* K, int S, int B,
                              const PhaseMap& phase, float* scores, void* ws, hipStream_t st);
 hipError_t launch_score_fp32(const Shape& s, const void* Q, const void* K, int S, int B,

@@ -695,7 +695,34 @@ WsLayout ws_layout(const Shape& s, int S, int B) {
   return w;
 }
 
+// Fixed device scratch of the allocation-free scoring entry point: the
+// scoring GEMM's partial block sums and range snapshots for shapes whose
+// workspace fits.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on a GPU shares it.  In host code `scratch` names
+// a host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress (score_scratch_ptr), per device.
+static __device__ __align__(256) unsigned char scratch[kScoreScratchBytes];
+
 }  // namespace
+
+hipError_t score_scratch_ptr(void** out) {
+  static std::atomic<void*> cached[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* ptr = cached[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    // once per device, with that device current; concurrent first calls all
+    // store the same address
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    cached[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
 
 size_t score_workspace_bytes(const Shape& s, int S, int B) {
   if (!s.bf16) return 0;

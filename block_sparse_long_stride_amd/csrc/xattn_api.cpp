@@ -149,6 +149,33 @@ xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
                    "xattn_score launch");
 }
 
+xattn_status xattn_score_noalloc(const xattn_shape* shape, const void* Q, const void* K,
+                                 int32_t S, int32_t B, float* scores, void* stream) {
+  static_assert(XATTN_SCORE_SCRATCH_BYTES == xattn::kScoreScratchBytes, "scratch size");
+  xattn::Shape s;
+  xattn_status st = check_score_args(shape, S, B, &s);
+  if (st != XATTN_OK) return st;
+  if (!Q || !K || !scores) return fail(XATTN_EINVAL, "Q, K and scores must be non-NULL");
+  st = check_aligned({Q, K, scores}, "Q, K, scores");
+  if (st != XATTN_OK) return st;
+  const size_t need = xattn::score_workspace_bytes(s, S, B);
+  if (need > xattn::kScoreScratchBytes)
+    return fail(XATTN_EWORKSPACE,
+                "xattn_score_noalloc: this shape needs %zu bytes of scoring scratch; the fixed "
+                "scratch holds %zu (use xattn_score with a caller workspace)",
+                need, xattn::kScoreScratchBytes);
+  hipStream_t hs = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (need) {
+    hipError_t e = xattn::score_scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_status(e, "xattn_score_noalloc scratch lookup");
+  }
+  xattn::PhaseMap antidiagonal{};
+  hipError_t e = s.bf16 ? xattn::launch_score_bf16(s, Q, K, S, B, antidiagonal, scores, ws, hs)
+                        : xattn::launch_score_fp32(s, Q, K, S, B, antidiagonal, scores, hs);
+  return hip_status(e, "xattn_score_noalloc launch");
+}
+
 xattn_status xattn_score_pattern(const xattn_shape* shape, const void* Q, const void* K,
                                  int32_t S, int32_t B, const int32_t* phase_host, float* scores,
                                  void* workspace, size_t workspace_bytes, void* stream) {

@@ -15,9 +15,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libxattn.so
 
 XATTN_OK, XATTN_EINVAL, XATTN_EUNSUPPORTED, XATTN_EWORKSPACE, XATTN_EHIP = range(5)
 XATTN_FP32, XATTN_BF16 = 0, 1
+XATTN_SCORE_SCRATCH_BYTES = 64 << 20   # fixed scratch of xattn_score_noalloc (include/xattn.h)
 
 # every entry point declared in include/xattn.h
-EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_score_pattern", "xattn_select",
+EXPORTS = ("xattn_score_workspace_bytes", "xattn_score", "xattn_score_noalloc",
+           "xattn_score_pattern", "xattn_select",
            "xattn_select_topk",
            "xattn_select_topratio", "xattn_score_select", "xattn_sparse_prefill", "xattn_full",
            "xattn_dit_workspace_bytes", "xattn_dit_attention", "xattn_head_error", "xattn_tau_dp",
@@ -53,6 +55,8 @@ def lib() -> ctypes.CDLL:
     L.xattn_score_workspace_bytes.restype = SZ
     L.xattn_score.argtypes = [SP, P, P, I32, I32, P, P, SZ, P]
     L.xattn_score.restype = I32
+    L.xattn_score_noalloc.argtypes = [SP, P, P, I32, I32, P, P]
+    L.xattn_score_noalloc.restype = I32
     L.xattn_score_pattern.argtypes = [SP, P, P, I32, I32, P, P, P, SZ, P]
     L.xattn_score_pattern.restype = I32
     L.xattn_select.argtypes = [I32, I32, I32, P, P, P, P, P, P]
@@ -172,6 +176,21 @@ def xattn_score(Q, K, S: int, B: int, causal: bool, scores=None, workspace=None,
                                          ph.ctypes.data_as(ctypes.c_void_p), _ptr(scores),
                                          _ptr(workspace), ws_bytes, _stream(stream)),
                "xattn_score_pattern")
+    return scores
+
+
+def xattn_score_noalloc(Q, K, S: int, B: int, causal: bool, scores=None, stream=None):
+    """Block scores through the library's fixed scratch (no workspace; the
+    caller may pass a preallocated `scores` to allocate nothing at all)."""
+    torch = _torch()
+    sh = shape_of(Q, K, causal)
+    NB = sh.L // B if B > 0 else 0
+    if scores is None:
+        scores = torch.empty((sh.hq, NB, NB), dtype=torch.float32, device=Q.device)
+    else:
+        _device_buffer(scores, "scores", (sh.hq, NB, NB), torch.float32, Q.device)
+    _check(lib().xattn_score_noalloc(ctypes.byref(sh), _ptr(Q), _ptr(K), S, B, _ptr(scores),
+                                     _stream(stream)), "xattn_score_noalloc")
     return scores
 
 

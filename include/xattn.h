@@ -10,6 +10,7 @@
  *
  * Calls, in the order of the path:
  *   xattn_score          block scores from strided antidiagonal sums
+ *   xattn_score_noalloc  the same with a fixed internal scratch (no workspace)
  *   xattn_score_pattern  block scores with another sampling pattern (ablation)
  *   xattn_select         threshold block selection -> mask, index lists
  *   xattn_select_topk    Top-K cut of the same ranking (selection ablation)
@@ -95,6 +96,26 @@ size_t xattn_score_workspace_bytes(const xattn_shape* shape, int32_t S, int32_t 
 xattn_status xattn_score(const xattn_shape* shape, const void* Q, const void* K,
                          int32_t S, int32_t B, float* scores, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/*
+ * xattn_score without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The scoring partials live in a fixed device array
+ * of XATTN_SCORE_SCRATCH_BYTES (64 MiB) inside the library, one copy on every
+ * GPU the library runs on, held until the process ends; the call allocates
+ * and frees nothing.  A shape whose xattn_score_workspace_bytes() exceeds it
+ * is refused with XATTN_EWORKSPACE before any device work (e.g. 32 query
+ * heads at L = 16384, S = 8, B = 128 need 50 MiB and fit; L = 32768 does not).
+ * The array keeps the last call's contents; nothing needs clearing, since a
+ * call rewrites every entry it reads.  All calls on one GPU share it: calls
+ * that overlap in time on one GPU (other streams, or other host threads
+ * without ordering) race and may return wrong scores; calls ordered on one
+ * stream are safe.  Scores are bit-identical to xattn_score's.  Arguments,
+ * outputs and other errors as xattn_score.
+ */
+#define XATTN_SCORE_SCRATCH_BYTES ((size_t)64 << 20)
+xattn_status xattn_score_noalloc(const xattn_shape* shape, const void* Q, const void* K,
+                                 int32_t S, int32_t B, float* scores, void* stream);
 
 /*
  * Block scores with another sampling pattern inside each SxS tile: the

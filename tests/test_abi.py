@@ -266,3 +266,23 @@ def test_fp32_sparse_prefill_bounds_its_lds_bitmap():
     assert lib.xattn_sparse_prefill(ctypes.byref(big), DUMMY, DUMMY, DUMMY, 1, DUMMY, DUMMY, DUMMY,
                                     None) == X.XATTN_EUNSUPPORTED
     assert b"LDS" in lib.xattn_last_error()
+
+
+def test_noalloc_score_refuses_shapes_beyond_its_scratch():
+    """xattn_score_noalloc works in a fixed 64 MiB device array: a shape whose
+    scoring workspace is larger is refused before any device work."""
+    lib = X.lib()
+    big = _shape(hq=32, hkv=8, L=32768)
+    need = lib.xattn_score_workspace_bytes(ctypes.byref(big), 8, 128)
+    assert need > 64 << 20
+    assert lib.xattn_score_noalloc(ctypes.byref(big), DUMMY, DUMMY, 8, 128, DUMMY,
+                                   None) == X.XATTN_EWORKSPACE
+    assert b"scratch" in lib.xattn_last_error()
+    fits = _shape(hq=32, hkv=8, L=16384)
+    assert lib.xattn_score_workspace_bytes(ctypes.byref(fits), 8, 128) <= 64 << 20
+    assert lib.xattn_score_noalloc(ctypes.byref(fits), MIS, DUMMY, 8, 128, DUMMY,
+                                   None) == X.XATTN_EINVAL
+    assert lib.xattn_score_noalloc(ctypes.byref(fits), DUMMY, DUMMY, 8, 100, DUMMY,
+                                   None) == X.XATTN_EINVAL
+    assert lib.xattn_score_noalloc(ctypes.byref(fits), DUMMY, None, 8, 128, DUMMY,
+                                   None) == X.XATTN_EINVAL
