@@ -189,6 +189,45 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
   const uint16_t* Kg = p.K + (size_t)g * p.L * D;
   const uint16_t* Vg = p.V + (size_t)g * p.L * D;
 
+  // The key blocks the workgroup visits: the union of the two blocks' sets,
+  // in ascending order, each with a flag per block.  Sparse mode builds it in
+  // LDS from the two lists (as bitmaps: invalid entries dropped, a repeated
+  // entry kept once); dense mode visits every causal-visible block.
+  //
+  // A wave's vector loads complete in order, so the two blocks' counts and
+  // index rows are requested together and before the query fragments: the
+  // bitmaps then wait for one memory round trip, not for the query loads
+  // issued ahead of them.  Rows of up to kRowAhead * threads entries are read
+  // whole (entries past the count are read and ignored); longer rows are read
+  // in a loop over their counted entries.
+  extern __shared__ int32_t s_dyn[];
+  const int nw32 = (p.NB + 31) / 32;
+  int32_t* s_list = s_dyn;                                  // [NB]: kb | flagA << 30 | flagB << 31
+  uint32_t* s_bits = (uint32_t*)(s_dyn + p.NB);             // [2][nw32]
+  int32_t* s_off = s_dyn + p.NB + 2 * nw32;                 // [nw32 + 1]
+  const bool sparse = p.idx != nullptr;
+  constexpr int kRowAhead = 4;
+  const bool whole_rows = p.NB <= kRowAhead * kThreads;
+  const bool hasB = qbB < p.NB;
+  const int32_t* rowA = p.idx + ((size_t)h * p.NB + qbA) * p.NB;
+  const int32_t* rowB = rowA + p.NB;
+  int cntA = 0, cntB = 0;
+  int ea[kRowAhead], eb[kRowAhead];
+  if (sparse) {
+    for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
+    cntA = p.counts[(size_t)h * p.NB + qbA];
+    cntB = hasB ? p.counts[(size_t)h * p.NB + qbB] : 0;
+    if (whole_rows) {
+#pragma unroll
+      for (int m = 0; m < kRowAhead; ++m) {
+        const int j = tid + m * kThreads;
+        ea[m] = j < p.NB ? rowA[j] : -1;
+        eb[m] = (hasB && j < p.NB) ? rowB[j] : -1;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");   // the query loads stay behind the index loads
+
   // query fragments (B operand of S^T = K Q^T): lane holds Q[qrow][16t + 8hi .. +8]
   bf16x8_t qf[D / 16];
   {
@@ -197,41 +236,52 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qp + 16 * t));
   }
 
-  // The key blocks the workgroup visits: the union of the two blocks' sets,
-  // in ascending order, each with a flag per block.  Sparse mode builds it in
-  // LDS from the two lists (as bitmaps: invalid entries dropped, a repeated
-  // entry kept once); dense mode visits every causal-visible block.
-  extern __shared__ int32_t s_dyn[];
-  const int nw32 = (p.NB + 31) / 32;
-  int32_t* s_list = s_dyn;                                  // [NB]: kb | flagA << 30 | flagB << 31
-  uint32_t* s_bits = (uint32_t*)(s_dyn + p.NB);             // [2][nw32]
-  int32_t* s_off = s_dyn + p.NB + 2 * nw32;                 // [nw32 + 1]
   int nkb;
-  const bool sparse = p.idx != nullptr;
   if (sparse) {
-    for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
-    __syncthreads();
+    cntA = cntA < 0 ? 0 : (cntA > p.NB ? p.NB : cntA);
+    cntB = cntB < 0 ? 0 : (cntB > p.NB ? p.NB : cntB);
+    __syncthreads();   // bitmaps cleared
+    auto mark = [&](int kb, int b, int qbb) __attribute__((always_inline)) {
+      if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) return;
+      atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
+    };
+    if (whole_rows) {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int qbb = qbA + b;
-      if (qbb >= p.NB) continue;
-      int cnt = p.counts[(size_t)h * p.NB + qbb];
-      cnt = cnt < 0 ? 0 : (cnt > p.NB ? p.NB : cnt);
-      const int32_t* list = p.idx + ((size_t)h * p.NB + qbb) * p.NB;
-      for (int j = tid; j < cnt; j += kThreads) {
-        const int kb = list[j];
-        if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) continue;
-        atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
+      for (int m = 0; m < kRowAhead; ++m) {
+        const int j = tid + m * kThreads;
+        if (j < cntA) mark(ea[m], 0, qbA);
+        if (j < cntB) mark(eb[m], 1, qbB);
       }
+    } else {
+      for (int j = tid; j < cntA; j += kThreads) mark(rowA[j], 0, qbA);
+      for (int j = tid; j < cntB; j += kThreads) mark(rowB[j], 1, qbB);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0;
-      for (int w = 0; w < nw32; ++w) {
-        s_off[w] = acc;
-        acc += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
+    // list offsets of the bitmap words: one wave, a few words per lane and a
+    // wave-wide inclusive scan of the per-lane counts
+    if (wave == 0) {
+      const int per = (nw32 + 63) / 64;
+      const int w0 = lane * per;
+      int c = 0;
+      for (int k = 0; k < per; ++k) {
+        const int w = w0 + k;
+        if (w < nw32) c += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
       }
-      s_off[nw32] = acc;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      int acc = incl - c;
+      for (int k = 0; k < per; ++k) {
+        const int w = w0 + k;
+        if (w < nw32) {
+          s_off[w] = acc;
+          acc += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
+        }
+      }
+      if (lane == 63) s_off[nw32] = incl;
     }
     __syncthreads();
     for (int w = tid; w < nw32; w += kThreads) {
