@@ -65,9 +65,6 @@ __device__ __forceinline__ int tile_off(int row, int col) {
   return row * (D * 2) + (((col >> 3) ^ swz<D>(row)) << 4) + ((col & 7) << 1);
 }
 
-// Copy one 64 x D tile (rows key0 .. key0+63 of src) into LDS by direct-to-LDS
-// loads.  Each instruction of a wave fills 1 KB of LDS in lane order; lane l
-// fetches the global chunk that the swizzled layout places at its position.
 // Keys per LDS tile: one whole 128-key block per step for B = 128 (half the
 // steps, barriers and per-step softmax overhead of 64-key tiles), 64 for B = 64.
 template <int BQ>
@@ -78,16 +75,23 @@ constexpr int kTileKeys = BQ >= 128 ? 128 : 64;
 // two and four pairs measure the same, one pair and eight or more are slower.
 constexpr int kPairsPerChunk = 2;
 
+// Copy one KT x D tile (rows key0 .. key0+KT-1 of one KV head's K or V) into
+// LDS by direct-to-LDS loads.  Each instruction of a wave fills 1 KB of LDS in
+// lane order; lane l fetches the global chunk that the swizzled layout places
+// at its position.  The loads go through a buffer resource over the head
+// (scalar tile offset, per-lane 32-bit offset fixed for the kernel): the
+// compiler counts the global-segment form of these loads as a possible LDS
+// access that completes out of order, so after it every wait for a fragment
+// read would drain all outstanding LDS reads; the buffer form keeps those
+// waits partial.
 template <int D, int KT, int NWAVES>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t* lds, int wave,
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t src, int key0, uint8_t* lds, int wave,
                                           int lane) {
   constexpr int kChunksPerRow = D / 8;
   constexpr int kRowsPerInst = 64 / kChunksPerRow;
   constexpr int kInsts = KT / kRowsPerInst;    // 1 KB instructions per tile
   static_assert(kInsts % NWAVES == 0, "tile instructions must split evenly over waves");
-  // uniform tile base (scalar) + per-lane 32-bit byte offset: the load uses
-  // the scalar-base addressing form, no 64-bit vector address math
-  const char* tile = (const char*)(src + (size_t)key0 * D);
+  const uint32_t tile = (uint32_t)key0 * (D * 2);
 #pragma unroll
   for (int k = 0; k < kInsts / NWAVES; ++k) {
     const int n = k * NWAVES + wave;               // wave is uniform (scalar)
@@ -95,9 +99,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int key0, uint8_t
     const int row = p / kChunksPerRow;
     const int c = (p % kChunksPerRow) ^ swz<D>(row);
     const uint32_t off = (uint32_t)(row * D * 2 + c * 16);
-    __builtin_amdgcn_global_load_lds((const void*)(tile + off),
-                                     (__attribute__((address_space(3))) void*)(lds + n * 1024),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void*)(lds + n * 1024),
+                                             16, off, tile, 0, 0);
   }
 }
 
@@ -186,8 +189,11 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
   const int qrow = qb * BQ + wq * 32 + l32;      // this lane's query token
   const int qwave0 = qb * BQ + wq * 32;
 
-  const uint16_t* Kg = p.K + (size_t)g * p.L * D;
-  const uint16_t* Vg = p.V + (size_t)g * p.L * D;
+  // this KV head's K and V as buffer resources (L * D * 2 < 2^31 bytes, checked by the caller)
+  const __amdgpu_buffer_rsrc_t Kg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.K + (size_t)g * p.L * D), (short)0, p.L * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t Vg = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.V + (size_t)g * p.L * D), (short)0, p.L * D * 2, 0x00020000);
 
   // The key blocks the workgroup visits: the union of the two blocks' sets,
   // in ascending order, each with a flag per block.  Sparse mode builds it in

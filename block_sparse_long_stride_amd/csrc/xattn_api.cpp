@@ -99,6 +99,10 @@ xattn_status check_attn_args(const xattn::Shape& s, int B) {
       return fail(XATTN_EUNSUPPORTED, "bf16 attention covers d in {64, 128}, got %d", s.d);
     if (B != 64 && B != 128)
       return fail(XATTN_EUNSUPPORTED, "bf16 attention covers B in {64, 128}, got %d", B);
+    // one KV head's K or V is addressed through a buffer resource of 32-bit size
+    if ((long long)s.L * s.d * 2 > 0x7FFFFFFFll)
+      return fail(XATTN_EUNSUPPORTED,
+                  "bf16 attention covers L * d * 2 < 2^31 bytes per head, got L=%d d=%d", s.L, s.d);
   } else {
     if (s.d != 32 && s.d != 64 && s.d != 128)
       return fail(XATTN_EUNSUPPORTED, "fp32 attention covers d in {32, 64, 128}, got %d", s.d);

@@ -275,8 +275,8 @@ xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const
  * causal-visible key block visited.
  *
  *   O  out, [hq][L][d] in the input dtype, fully overwritten.
- * bf16 kernels need L % 64 == 0 and d in {64, 128}; fp32 kernels cover
- * d in {32, 64, 128} (else XATTN_EUNSUPPORTED).
+ * bf16 kernels need L % 64 == 0, d in {64, 128} and L * d * 2 < 2^31 bytes
+ * per head; fp32 kernels cover d in {32, 64, 128} (else XATTN_EUNSUPPORTED).
  */
 xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K,
                         const void* V, void* O, void* stream);

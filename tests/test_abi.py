@@ -70,6 +70,13 @@ def test_score_rejects_heads_beyond_32_bit_buffers():
     assert b"2^31" in lib.xattn_last_error()
 
 
+def test_attention_rejects_heads_beyond_32_bit_buffers():
+    lib = X.lib()
+    sh = _shape(hq=1, hkv=1, L=1 << 23, d=128)   # 2^31 bytes per KV head
+    assert lib.xattn_full(ctypes.byref(sh), DUMMY, DUMMY, DUMMY, DUMMY, None) == X.XATTN_EUNSUPPORTED
+    assert b"2^31" in lib.xattn_last_error()
+
+
 def test_score_workspace_checks():
     lib = X.lib()
     sh = _shape()
