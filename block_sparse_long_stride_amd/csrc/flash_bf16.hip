@@ -41,7 +41,7 @@ struct FlashParams {
   const int32_t* idx;      // nullptr: dense
   const int32_t* counts;
   int L, hq, group, NB, causal;
-  int nwork, grid, interleave;
+  int nwork, grid, interleave, chunk_pairs;
   float scale_log2;        // log2(e) / sqrt(d)
 };
 
@@ -71,9 +71,14 @@ template <int BQ>
 constexpr int kTileKeys = BQ >= 128 ? 128 : 64;
 
 // Query-block pairs per scheduling chunk (times the heads of a KV group).
-// Small chunks keep the work per XCD even; with the alternating deal below,
-// two and four pairs measure the same, one pair and eight or more are slower.
-constexpr int kPairsPerChunk = 2;
+// The work-groups of one chunk share their key/value tiles in the XCD's L2,
+// so larger chunks fetch fewer bytes beyond it; small chunks keep the work
+// per XCD even.  With the alternating deal below, from 512 pairs per head on
+// eight pairs fetch 17 % fewer bytes than two (131K tokens: 107 against
+// 129 GB per sparse launch, 18.5 against 36 GB dense) in the same time; at 128
+// pairs per head eight are 3.5 % slower than two, and sixteen are slower at
+// every size measured.
+inline int pairs_per_chunk(int npairs) { return npairs >= 512 ? 8 : 2; }
 
 // Copy one KT x D tile (rows key0 .. key0+KT-1 of one KV head's K or V) into
 // LDS by direct-to-LDS loads.  Each instruction of a wave fills 1 KB of LDS in
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
 
   // Work order.  A work item is a pair of neighbouring query blocks (2i,
   // 2i+1) of one head.  Items of one KV group are (pair descending, head),
-  // cut into chunks of kPairsPerChunk pairs x all heads of the group.
+  // cut into chunks of p.chunk_pairs pairs x all heads of the group.
   // Chunks are dealt to the 8 XCDs in rounds of eight, the XCD order
   // reversed every other round, and every XCD runs through the groups in
   // the same order, so (a) all XCDs work on the same KV group at a time --
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     const int bid = blockIdx.x;
     const int xcd = bid % kNumXcd, k = bid / kNumXcd;
     const int per_xcd = per_group / kNumXcd;     // items of one group on one XCD
-    const int chunk = kPairsPerChunk * p.group;  // items per chunk
+    const int chunk = p.chunk_pairs * p.group;   // items per chunk
     g = k / per_xcd;
     const int kk = k % per_xcd;
     const int r = kk / chunk;                    // round
@@ -555,7 +560,8 @@ hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const
   const int npairs = (fp.NB + 1) / 2;
   fp.nwork = npairs * s.hq;
   fp.grid = (fp.nwork + kNumXcd - 1) / kNumXcd * kNumXcd;
-  fp.interleave = (npairs * fp.group) % (kNumXcd * kPairsPerChunk * fp.group) == 0;
+  fp.chunk_pairs = pairs_per_chunk(npairs);
+  fp.interleave = (npairs * fp.group) % (kNumXcd * fp.chunk_pairs * fp.group) == 0;
   fp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
   if (s.d == 128) return B == 128 ? launch<128, 128>(fp, st) : launch<128, 64>(fp, st);
   return B == 128 ? launch<64, 128>(fp, st) : launch<64, 64>(fp, st);
