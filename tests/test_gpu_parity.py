@@ -30,6 +30,11 @@ SMALL = {
     # and L/S = 528, a ragged last scoring tile
     "llm-odd-blocks": get_config(2, hq=2, hkv=1, L=4224),
     "noncausal-llm-fp32": get_config(1, causal=False, L=1024),
+    # fp32 attention: a block size that is not a multiple of 32 (the SIMT
+    # kernel) at d = 32, and one of three 32-row waves (the matrix-core
+    # kernel) at d = 128
+    "fp32-B48-d32": get_config(1, L=1536, B=48, S=8, d=32),
+    "fp32-B96-d128": get_config(1, L=1536, B=96, S=8, d=128),
     # the attention kernel's interleaved XCD work order (pairs of query blocks
     # a multiple of 16), two rounds of chunks per XCD so the alternating deal
     # is used, with one and with eight query heads per KV head
