@@ -380,6 +380,12 @@ def main():
 
     tflops = F_full / (wall_ms * 1e-3) / 1e12
     achieved = F_sparse / (sparse_ms * 1e-3) / 1e12
+    # the library runs bf16 sparse prefill persistent while an index row has at
+    # most four entries per thread (NB <= 16 B), one work-group per item beyond
+    if cfg.dtype == "bf16":
+        sparse_kernel = "flash_bf16_persistent_kernel" if NB <= 16 * cfg.B else "flash_bf16_kernel"
+    else:
+        sparse_kernel = "flash_fp32_mfma_kernel" if cfg.B % 32 == 0 else "flash_fp32_kernel"
     res = {
         "metric": "score+select+sparse-prefill ms and dense-equiv TFLOP/s at L=128K, 32/8 heads",
         "value": round(tflops, 2),
@@ -417,7 +423,7 @@ def main():
                 "tflops": round(F_full / (full_ms * 1e-3) / 1e12, 1),
                 "frac_bf16_peak": round(F_full / (full_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
         },
-        "roofline": {"bound": "mfma", "kernel": "flash_bf16_kernel (xattn_sparse_prefill)",
+        "roofline": {"bound": "mfma", "kernel": f"{sparse_kernel} (xattn_sparse_prefill)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic("flash_bf16", f"config{cfg.cid}")},

@@ -21,6 +21,8 @@
 // bf16, and accumulates O^T += V^T P^T.  The V^T operand comes from the
 // row-major V tile through LDS transpose reads (ds_read_b64_tr_b16).  Query
 // head h reads key/value head h / (hq / hkv).
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -43,6 +45,7 @@ struct FlashParams {
   int L, hq, group, NB, causal;
   int nwork, grid, interleave, chunk_pairs;
   float scale_log2;        // log2(e) / sqrt(d)
+  unsigned int* queue;     // persistent sparse mode: this launch's per-XCD item counters
 };
 
 // XOR swizzle of the 16-byte chunks of a tile row: chunk c of row r sits at
@@ -126,6 +129,190 @@ __device__ __forceinline__ float max_with_other_half(float x) {
 
 __device__ __forceinline__ uint32_t cvt2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// One wave's share of a key/value tile: kKT keys from key0 (rows of sK, sV)
+// against its 32 query rows (this lane: row qrow; the wave's first row is
+// qwave0), folded into the running output o, row max m and denominator
+// share lsum.
+template <int D, int kKT>
+__device__ __forceinline__ void attend_tile(float scale_log2, int causal, const uint8_t* sK, const uint8_t* sV,
+                                            const int (&koff)[D / 16], const int (&voff)[D / 32][2],
+                                            const bf16x8_t (&qf)[D / 16], f32x16_t (&o)[D / 32],
+                                            float& m, float& lsum, int key0, int qrow, int qwave0,
+                                            int hi) {
+  // S^T (kKT keys x 32 queries) as kNS 32x32 tiles.  K fragments are read
+  // kAhead k-steps before their MFMAs so LDS latency overlaps the matrix
+  // work instead of stalling each MFMA.
+  constexpr int kSteps = D / 16;
+  constexpr int kNS = kKT / 32;                // 32-key sub-tiles
+  constexpr int kNU = kKT / 16;                // 16-key chunks of P
+  constexpr int kAhead = kNS >= 4 ? 2 : 3;
+  f32x16_t s[kNS];
+#pragma unroll
+  for (int i = 0; i < kNS; ++i) s[i] = f32x16_t{};
+  bf16x8_t kfr[kAhead + 1][kNS];
+#pragma unroll
+  for (int t = 0; t < kAhead; ++t)
+#pragma unroll
+    for (int i = 0; i < kNS; ++i)
+      kfr[t][i] = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
+#pragma unroll
+  for (int t = 0; t < kSteps; ++t) {
+    if (t + kAhead < kSteps) {
+#pragma unroll
+      for (int i = 0; i < kNS; ++i)
+        kfr[(t + kAhead) % (kAhead + 1)][i] =
+            as_bf16x8(*(const u32x4_t*)(sK + koff[t + kAhead] + i * 32 * D * 2));
+    }
+#pragma unroll
+    for (int i = 0; i < kNS; ++i) s[i] = mfma_32x32x16(kfr[t % (kAhead + 1)][i], qf[t], s[i]);
+  }
+  // Keep the reads kAhead steps ahead: the scheduler otherwise sinks them
+  // next to their MFMAs.  (mask 0x100: DS read, 0x008: MFMA)
+  __builtin_amdgcn_sched_group_barrier(0x100, kNS * kAhead, 0);
+#pragma unroll
+  for (int t = 0; t < kSteps - kAhead; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kNS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kNS, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kNS * kAhead, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  // V^T fragments (A operand of O^T += V^T P^T) of 16-key chunk u and
+  // output column block dt, by transposed LDS reads; chunk 0 is read now
+  // so the reads land during the softmax.
+  auto read_v = [&](int u, int dt) -> bf16x8_t {
+    const uint8_t* vp = sV + 16 * u * D * 2;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][0]));
+    const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][1]));
+    return as_bf16x8(u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                             __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]});
+  };
+  bf16x8_t vf[2][D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) vf[0][dt] = read_v(0, dt);
+  __builtin_amdgcn_sched_barrier(0);
+  if (causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
+    // key = key0 + 4 hi + (32 i + 8 (v / 4) + v % 4) is masked when it
+    // exceeds qrow: one per-lane bound against compile-time offsets (no
+    // per-element key constants held in registers across the loop)
+    const int bound = qrow - key0 - 4 * hi;
+#pragma unroll
+    for (int i = 0; i < kNS; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (32 * i + 8 * (v >> 2) + (v & 3) > bound) s[i][v] = -INFINITY;
+  }
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kNS; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
+  mloc = max_with_other_half(mloc) * scale_log2;
+  // The reference max m of a row only moves when this tile's max exceeds it
+  // by more than kSlack (log2 units), so P stays <= 2^kSlack and the O /
+  // denominator rescale (a wave-uniform branch) is rare.  The result is
+  // unchanged: numerator and denominator share the reference.  A row with
+  // nothing visible yet keeps m = -inf and gets p = 0.
+  constexpr float kSlack = 8.0f;
+  if (__ballot(mloc > m + kSlack)) {
+    const float mnew = (mloc > m + kSlack) ? mloc : m;
+    const float alpha = fast_exp2(m - mnew);   // m == -inf gives 0; unchanged rows 1
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+    m = mnew;
+  }
+  const float mref = (m == -INFINITY) ? 0.f : m;
+  // P in bf16 in chunks of 16 keys; the denominator sums the same
+  // rounded values (packed dot2, in chunk order).  The MFMAs of chunk u
+  // are interleaved with the exponentials and V reads of chunk u + 1
+  // (fenced, so the vector and matrix work of one wave overlap).
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rs0 = 0.f, rs1 = 0.f;
+  auto p_pair = [&](int u, int e) -> uint32_t {
+    const int i = u >> 1, v0 = (u & 1) * 8;
+    const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], scale_log2, -mref));
+    const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], scale_log2, -mref));
+    const uint32_t pk = cvt2_bf16(p0, p1);
+    if (e & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs1, false);
+    else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs0, false);
+    return pk;
+  };
+  constexpr int kDt = D / 32;            // output column blocks
+  constexpr int kPairsPerDt = 4 / kDt;   // P pairs of the next chunk per MFMA
+  uint32_t pk[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pk[e] = p_pair(0, e);
+  bf16x8_t pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+  for (int u = 0; u < kNU; ++u) {
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      o[dt] = mfma_32x32x16(vf[u & 1][dt], pcur, o[dt]);
+      if (u < kNU - 1) {
+        vf[(u + 1) & 1][dt] = read_v(u + 1, dt);
+#pragma unroll
+        for (int e = dt * kPairsPerDt; e < (dt + 1) * kPairsPerDt; ++e) pk[e] = p_pair(u + 1, e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (u < kNU - 1) pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+  }
+  lsum += rs0 + rs1;
+}
+
+// The merged key-block list of a work item from the two blocks' bitmaps
+// (s_bits[0 .. nw32) for the first block, s_bits[nw32 .. 2 nw32) for the
+// second): entry kb | flagA << 30 | flagB << 31 in ascending kb, written to
+// s_list with the per-word offsets in s_off; the entry count is s_off[nw32]
+// after the final barrier.  With `clear` the bitmap words are zeroed as they
+// are consumed, ready for the next item.  All threads call it (barriers).
+template <int kThreads>
+__device__ __forceinline__ void finish_list(uint32_t* s_bits, int32_t* s_off, int32_t* s_list, int nw32,
+                                            int tid, int wave, int lane, bool clear) {
+  // list offsets of the bitmap words: one wave, a few words per lane and a
+  // wave-wide inclusive scan of the per-lane counts
+  if (wave == 0) {
+    const int per = (nw32 + 63) / 64;
+    const int w0 = lane * per;
+    int c = 0;
+    for (int k = 0; k < per; ++k) {
+      const int w = w0 + k;
+      if (w < nw32) c += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
+    }
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    int acc = incl - c;
+    for (int k = 0; k < per; ++k) {
+      const int w = w0 + k;
+      if (w < nw32) {
+        s_off[w] = acc;
+        acc += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
+      }
+    }
+    if (lane == 63) s_off[nw32] = incl;
+  }
+  __syncthreads();
+  for (int w = tid; w < nw32; w += kThreads) {
+    const uint32_t a = s_bits[w], bb = s_bits[nw32 + w];
+    if (clear) {
+      s_bits[w] = 0u;
+      s_bits[nw32 + w] = 0u;
+    }
+    uint32_t u = a | bb;
+    int o = s_off[w];
+    while (u) {
+      const int bit = __builtin_ctz(u);
+      s_list[o++] = (int32_t)((uint32_t)(32 * w + bit) | (((a >> bit) & 1u) << 30) | (((bb >> bit) & 1u) << 31));
+      u &= u - 1;
+    }
+  }
+  __syncthreads();
 }
 
 template <int D, int BQ>
@@ -268,45 +455,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       for (int j = tid; j < cntB; j += kThreads) mark(rowB[j], 1, qbB);
     }
     __syncthreads();
-    // list offsets of the bitmap words: one wave, a few words per lane and a
-    // wave-wide inclusive scan of the per-lane counts
-    if (wave == 0) {
-      const int per = (nw32 + 63) / 64;
-      const int w0 = lane * per;
-      int c = 0;
-      for (int k = 0; k < per; ++k) {
-        const int w = w0 + k;
-        if (w < nw32) c += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
-      }
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      int acc = incl - c;
-      for (int k = 0; k < per; ++k) {
-        const int w = w0 + k;
-        if (w < nw32) {
-          s_off[w] = acc;
-          acc += __builtin_popcount(s_bits[w] | s_bits[nw32 + w]);
-        }
-      }
-      if (lane == 63) s_off[nw32] = incl;
-    }
-    __syncthreads();
-    for (int w = tid; w < nw32; w += kThreads) {
-      const uint32_t a = s_bits[w], bb = s_bits[nw32 + w];
-      uint32_t u = a | bb;
-      int o = s_off[w];
-      while (u) {
-        const int bit = __builtin_ctz(u);
-        s_list[o++] = (int32_t)((uint32_t)(32 * w + bit) | (((a >> bit) & 1u) << 30) | (((bb >> bit) & 1u) << 31));
-        u &= u - 1;
-      }
-    }
+    finish_list<kThreads>(s_bits, s_off, s_list, nw32, tid, wave, lane, false);
     nkb = s_off[nw32];
-    __syncthreads();
   } else {
     nkb = p.causal ? min(qbB, p.NB - 1) + 1 : p.NB;
   }
@@ -374,125 +524,7 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
       load_tile<D, kKT, kWaves>(Vg, key0_next, nV, wave, lane);
     }
     if (key0 >= 0 && mine && !(p.causal && key0 > qwave0 + 31)) {
-      // S^T (kKT keys x 32 queries) as kNS 32x32 tiles.  K fragments are read
-      // kAhead k-steps before their MFMAs so LDS latency overlaps the matrix
-      // work instead of stalling each MFMA.
-      constexpr int kSteps = D / 16;
-      constexpr int kNS = kKT / 32;                // 32-key sub-tiles
-      constexpr int kNU = kKT / 16;                // 16-key chunks of P
-      constexpr int kAhead = kNS >= 4 ? 2 : 3;
-      f32x16_t s[kNS];
-#pragma unroll
-      for (int i = 0; i < kNS; ++i) s[i] = f32x16_t{};
-      bf16x8_t kfr[kAhead + 1][kNS];
-#pragma unroll
-      for (int t = 0; t < kAhead; ++t)
-#pragma unroll
-        for (int i = 0; i < kNS; ++i)
-          kfr[t][i] = as_bf16x8(*(const u32x4_t*)(sK + koff[t] + i * 32 * D * 2));
-#pragma unroll
-      for (int t = 0; t < kSteps; ++t) {
-        if (t + kAhead < kSteps) {
-#pragma unroll
-          for (int i = 0; i < kNS; ++i)
-            kfr[(t + kAhead) % (kAhead + 1)][i] =
-                as_bf16x8(*(const u32x4_t*)(sK + koff[t + kAhead] + i * 32 * D * 2));
-        }
-#pragma unroll
-        for (int i = 0; i < kNS; ++i) s[i] = mfma_32x32x16(kfr[t % (kAhead + 1)][i], qf[t], s[i]);
-      }
-      // Keep the reads kAhead steps ahead: the scheduler otherwise sinks them
-      // next to their MFMAs.  (mask 0x100: DS read, 0x008: MFMA)
-      __builtin_amdgcn_sched_group_barrier(0x100, kNS * kAhead, 0);
-#pragma unroll
-      for (int t = 0; t < kSteps - kAhead; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, kNS, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, kNS, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kNS * kAhead, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // V^T fragments (A operand of O^T += V^T P^T) of 16-key chunk u and
-      // output column block dt, by transposed LDS reads; chunk 0 is read now
-      // so the reads land during the softmax.
-      auto read_v = [&](int u, int dt) -> bf16x8_t {
-        const uint8_t* vp = sV + 16 * u * D * 2;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][0]));
-        const v4i16 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + voff[dt][1]));
-        return as_bf16x8(u32x4_t{__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                                 __builtin_bit_cast(u32x2_t, hi4)[0], __builtin_bit_cast(u32x2_t, hi4)[1]});
-      };
-      bf16x8_t vf[2][D / 32];
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) vf[0][dt] = read_v(0, dt);
-      __builtin_amdgcn_sched_barrier(0);
-      if (p.causal && key0 + kKT - 1 > qwave0) {   // tile crosses this wave's diagonal
-        // key = key0 + 4 hi + (32 i + 8 (v / 4) + v % 4) is masked when it
-        // exceeds qrow: one per-lane bound against compile-time offsets (no
-        // per-element key constants held in registers across the loop)
-        const int bound = qrow - key0 - 4 * hi;
-#pragma unroll
-        for (int i = 0; i < kNS; ++i)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (32 * i + 8 * (v >> 2) + (v & 3) > bound) s[i][v] = -INFINITY;
-      }
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < kNS; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mloc = fmaxf(mloc, s[i][v]);
-      mloc = max_with_other_half(mloc) * p.scale_log2;
-      // The reference max m of a row only moves when this tile's max exceeds it
-      // by more than kSlack (log2 units), so P stays <= 2^kSlack and the O /
-      // denominator rescale (a wave-uniform branch) is rare.  The result is
-      // unchanged: numerator and denominator share the reference.  A row with
-      // nothing visible yet keeps m = -inf and gets p = 0.
-      constexpr float kSlack = 8.0f;
-      if (__ballot(mloc > m + kSlack)) {
-        const float mnew = (mloc > m + kSlack) ? mloc : m;
-        const float alpha = fast_exp2(m - mnew);   // m == -inf gives 0; unchanged rows 1
-        lsum *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-        m = mnew;
-      }
-      const float mref = (m == -INFINITY) ? 0.f : m;
-      // P in bf16 in chunks of 16 keys; the denominator sums the same
-      // rounded values (packed dot2, in chunk order).  The MFMAs of chunk u
-      // are interleaved with the exponentials and V reads of chunk u + 1
-      // (fenced, so the vector and matrix work of one wave overlap).
-      const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float rs0 = 0.f, rs1 = 0.f;
-      auto p_pair = [&](int u, int e) -> uint32_t {
-        const int i = u >> 1, v0 = (u & 1) * 8;
-        const float p0 = fast_exp2(fmaf(s[i][v0 + 2 * e], p.scale_log2, -mref));
-        const float p1 = fast_exp2(fmaf(s[i][v0 + 2 * e + 1], p.scale_log2, -mref));
-        const uint32_t pk = cvt2_bf16(p0, p1);
-        if (e & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs1, false);
-        else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, rs0, false);
-        return pk;
-      };
-      constexpr int kDt = D / 32;            // output column blocks
-      constexpr int kPairsPerDt = 4 / kDt;   // P pairs of the next chunk per MFMA
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pk[e] = p_pair(0, e);
-      bf16x8_t pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-      for (int u = 0; u < kNU; ++u) {
-#pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) {
-          o[dt] = mfma_32x32x16(vf[u & 1][dt], pcur, o[dt]);
-          if (u < kNU - 1) {
-            vf[(u + 1) & 1][dt] = read_v(u + 1, dt);
-#pragma unroll
-            for (int e = dt * kPairsPerDt; e < (dt + 1) * kPairsPerDt; ++e) pk[e] = p_pair(u + 1, e);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (u < kNU - 1) pcur = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-      }
-      lsum += rs0 + rs1;
+      attend_tile<D, kKT>(p.scale_log2, p.causal, sK, sV, koff, voff, qf, o, m, lsum, key0, qrow, qwave0, hi);
     }
     key0 = key0_next;
     mine = mine_next;
@@ -521,15 +553,349 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_kernel(FlashParams p) {
     }
 }
 
+// Work queues of the persistent sparse kernel: kQueueSlots launch slots of
+// one counter per XCD, each counter on its own 128-byte line.  A launch takes
+// the next slot (round robin on the host) and clears it with a kernel on its
+// own stream first, so calls may overlap on one GPU as long as fewer than
+// kQueueSlots of them are in flight at once.  In host code `attn_queue` names
+// a host-side stand-in; its device address comes from hipGetSymbolAddress,
+// per device.
+constexpr int kQueueSlots = 64;
+constexpr int kQueueStride = 32;   // unsigned ints per counter (128 bytes)
+static __device__ __align__(256) unsigned int attn_queue[kQueueSlots * kNumXcd * kQueueStride];
+
+__global__ void queue_reset_kernel(unsigned int* q) {
+  if (threadIdx.x < kNumXcd) q[threadIdx.x * kQueueStride] = 0u;
+}
+
+// Work item k of XCD xcd in the order the non-persistent grid dispatches
+// them: KV group g and the item's index rem within the group.
+__device__ __forceinline__ void decode_item(const FlashParams& p, int xcd, int k, int& g, int& rem) {
+  const int per_group = ((p.NB + 1) / 2) * p.group;
+  if (p.interleave) {
+    const int per_xcd = per_group / kNumXcd;
+    const int chunk = p.chunk_pairs * p.group;
+    g = k / per_xcd;
+    const int kk = k % per_xcd;
+    const int r = kk / chunk;
+    rem = (r * kNumXcd + ((r & 1) ? kNumXcd - 1 - xcd : xcd)) * chunk + kk % chunk;
+  } else {
+    const int w = xcd * ((p.nwork + kNumXcd - 1) / kNumXcd) + k;
+    g = w / per_group;
+    rem = w % per_group;
+  }
+}
+
+// Number of work items of XCD xcd.
+__device__ __forceinline__ int items_on_xcd(const FlashParams& p, int xcd) {
+  if (p.interleave) return (((p.NB + 1) / 2) * p.group / kNumXcd) * (p.hq / p.group);
+  const int per = (p.nwork + kNumXcd - 1) / kNumXcd;
+  return max(0, min(per, p.nwork - xcd * per));
+}
+
+// Index rows held whole in the persistent kernel's stage: kRowAhead entries
+// per thread.
+constexpr int kRowAhead = 4;
+
+// A work item of the persistent kernel: (queue << 24) | index in that queue.
+constexpr int kNoItem = -1;
+
+// Persistent form of the sparse mode, for index rows of at most kRowAhead x
+// threads entries.  One work-group per CU takes the work items of its XCD
+// from a counter, in the non-persistent kernel's order; once that queue is
+// empty it takes the remaining items of the other XCDs' queues, so the load
+// stays balanced as with hardware dispatch.  What a work-group otherwise
+// pays at each start is hidden: near the end of item i the next item is
+// claimed and its index rows and counts are copied into LDS by direct-to-LDS
+// loads, so between two items only the list build from LDS, the query loads
+// and the first tile's copy remain.  Items, tiles and arithmetic are
+// those of the non-persistent kernel.
+template <int D, int BQ>
+__global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashParams p) {
+  constexpr int kBlockWaves = BQ / 32;
+  constexpr int kWaves = 2 * kBlockWaves;
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kKT = kTileKeys<BQ>;
+  constexpr int kTilesPerBlock = BQ / kKT;
+  constexpr int kTileBytes = kKT * D * 2;
+  constexpr int kStageInts = 2 * kRowAhead * kThreads;
+  __shared__ __attribute__((aligned(1024))) uint8_t sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
+  // the next item's two index rows (adjacent in memory, copied as one run)
+  // and its two counts; every lane of a copy writes, so the counts take 64
+  __shared__ __attribute__((aligned(256))) int32_t s_stage[kStageInts];
+  __shared__ __attribute__((aligned(256))) int32_t s_stage_cnt[64];
+  __shared__ int s_next[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int half = wave / kBlockWaves;           // 0: first block of the pair, 1: second
+  const int wq = wave % kBlockWaves;
+  const int xcd = blockIdx.x % kNumXcd;
+  const int npairs = (p.NB + 1) / 2;
+
+  extern __shared__ int32_t s_dyn[];
+  const int nw32 = (p.NB + 31) / 32;
+  int32_t* s_list = s_dyn;                                  // [NB]: kb | flagA << 30 | flagB << 31
+  uint32_t* s_bits = (uint32_t*)(s_dyn + p.NB);             // [2][nw32]
+  int32_t* s_off = s_dyn + p.NB + 2 * nw32;                 // [nw32 + 1]
+
+  int koff[D / 16], voff[D / 32][2];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) koff[t] = tile_off<D>(l32, 16 * t + 8 * hi);
+    const int vrow = 4 * hi + (i16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        voff[dt][r] = tile_off<D>(vrow + 8 * r, 32 * dt + 16 * (g16 & 1) + 4 * (i16 & 3));
+  }
+
+  // thread 0: the next item of this XCD's queue or, once that is empty, of
+  // the other queues in turn, starting from the one the last item came
+  // from; kNoItem when every queue is empty.  Every item is handed out by
+  // exactly one counter increment.
+  int q_from = xcd;
+  auto fetch = [&]() __attribute__((always_inline)) -> int {
+    for (int t = 0; t < kNumXcd; ++t) {
+      const int xq = (q_from + t) % kNumXcd;
+      const int k = (int)atomicAdd(p.queue + xq * kQueueStride, 1u);
+      if (k < items_on_xcd(p, xq)) {
+        q_from = xq;
+        return (xq << 24) | k;
+      }
+    }
+    return kNoItem;
+  };
+  // head and first query block of an item
+  auto locate = [&](int item, int& g, int& h, int& qbA) __attribute__((always_inline)) {
+    int rem;
+    decode_item(p, item >> 24, item & 0xFFFFFF, g, rem);
+    qbA = 2 * (npairs - 1 - rem / p.group);
+    h = g * p.group + rem % p.group;
+  };
+  // copy item k's index rows and counts into the stage
+  auto stage = [&](int k) __attribute__((always_inline)) {
+    int g, h, qbA;
+    locate(k, g, h, qbA);
+    const int rows = qbA + 1 < p.NB ? 2 : 1;
+    const int n = rows * p.NB;
+    const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.idx + ((size_t)h * p.NB + qbA) * p.NB), (short)0, n * 4, 0x00020000);
+    for (int i = wave; i < (n + 63) / 64; i += kWaves)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (__attribute__((address_space(3))) void*)(s_stage + i * 64),
+                                               4, lane * 4, i * 256, 0, 0);
+    if (wave == kWaves - 1) {
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.counts + (size_t)h * p.NB + qbA), (short)0, rows * 4, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)s_stage_cnt, 4,
+                                               lane * 4, 0, 0, 0);
+    }
+  };
+  // the merged list of item k from the stage (the bitmaps are clear on entry
+  // and cleared again as the list is written); returns the entry count
+  auto build_list = [&](int k) __attribute__((always_inline)) -> int {
+    int g, h, qbA;
+    locate(k, g, h, qbA);
+    const int qbB = qbA + 1;
+    int cntA = s_stage_cnt[0];
+    int cntB = qbB < p.NB ? s_stage_cnt[1] : 0;
+    cntA = cntA < 0 ? 0 : (cntA > p.NB ? p.NB : cntA);
+    cntB = cntB < 0 ? 0 : (cntB > p.NB ? p.NB : cntB);
+    auto mark = [&](int kb, int b, int qbb) __attribute__((always_inline)) {
+      if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) return;
+      atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
+    };
+#pragma unroll
+    for (int m = 0; m < kRowAhead; ++m) {
+      const int j = tid + m * kThreads;
+      if (j < cntA) mark(s_stage[j], 0, qbA);
+      if (j < cntB) mark(s_stage[p.NB + j], 1, qbB);
+    }
+    __syncthreads();
+    finish_list<kThreads>(s_bits, s_off, s_list, nw32, tid, wave, lane, true);
+    return s_off[nw32];
+  };
+
+  // The first item; its number reaches every thread through LDS.  Each later
+  // item is claimed kClaimAhead tiles before the current one ends, about
+  // when a non-persistent work-group would start on this CU, so items go to
+  // whichever CU frees up first; its index rows are copied into the stage
+  // during the tile after the claim.
+  constexpr int kClaimAhead = 3;
+  if (tid == 0) s_next[0] = fetch();
+  for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(s_next[0]);
+  if (cur == kNoItem) return;
+  stage(cur);
+  wait_vmem();
+  __syncthreads();
+  int nkb = build_list(cur);
+
+  for (;;) {
+    int g, h, qbA;
+    locate(cur, g, h, qbA);
+    const int qb = qbA + half;
+    const bool rows_valid = qb < p.NB;
+    const int qrow = qb * BQ + wq * 32 + l32;
+    const int qwave0 = qb * BQ + wq * 32;
+    const __amdgpu_buffer_rsrc_t Kg = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.K + (size_t)g * p.L * D), (short)0, p.L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t Vg = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.V + (size_t)g * p.L * D), (short)0, p.L * D * 2, 0x00020000);
+
+    bf16x8_t qf[D / 16];
+    {
+      const uint16_t* qp = p.Q + ((size_t)h * p.L + (rows_valid ? qrow : qrow - BQ)) * D + hi * 8;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qp + 16 * t));
+    }
+
+    const int ntiles = nkb * kTilesPerBlock;
+    auto tile_info = [&](int n, bool& mine) -> int {
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_list[n / kTilesPerBlock]);
+      mine = half ? (e >> 31) : ((e >> 30) & 1u);
+      return (int)(e & 0x3FFFFFFFu) * BQ + (n % kTilesPerBlock) * kKT;
+    };
+
+    f32x16_t o[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) o[i] = f32x16_t{};
+    float m = -INFINITY;
+    float lsum = 0.f;
+
+    // tile n_claim claims the next item (thread 0, at the tile's end), tile
+    // n_claim + 1 copies its rows and counts into the stage
+    const int n_claim = ntiles > kClaimAhead ? ntiles - kClaimAhead : 0;
+    int nxt = kNoItem;
+    bool staged = false;
+
+    bool mine = false;
+    int key0 = ntiles > 0 ? tile_info(0, mine) : -1;
+    if (key0 >= 0) {
+      load_tile<D, kKT, kWaves>(Kg, key0, sK0, wave, lane);
+      load_tile<D, kKT, kWaves>(Vg, key0, sV0, wave, lane);
+    }
+    wait_vmem();
+    __syncthreads();
+
+    auto step = [&](int n, const uint8_t* sK, const uint8_t* sV, uint8_t* nK,
+                    uint8_t* nV) __attribute__((always_inline)) {
+      bool mine_next = false;
+      const int key0_next = (n + 1 < ntiles) ? tile_info(n + 1, mine_next) : -1;
+      if (key0_next >= 0) {
+        load_tile<D, kKT, kWaves>(Kg, key0_next, nK, wave, lane);
+        load_tile<D, kKT, kWaves>(Vg, key0_next, nV, wave, lane);
+      }
+      if (n == n_claim + 1) {
+        nxt = __builtin_amdgcn_readfirstlane(s_next[0]);
+        if (nxt != kNoItem) stage(nxt);
+        staged = true;
+      }
+      if (key0 >= 0 && mine && !(p.causal && key0 > qwave0 + 31))
+        attend_tile<D, kKT>(p.scale_log2, p.causal, sK, sV, koff, voff, qf, o, m, lsum, key0, qrow, qwave0, hi);
+      key0 = key0_next;
+      mine = mine_next;
+      // the compiler waits for an atomic's result at once: here that falls
+      // inside the wait for the next tile
+      if (n == n_claim && tid == 0) s_next[0] = fetch();
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int n = 0; n < ntiles; n += 2) {
+      step(n, sK0, sV0, sK1, sV1);
+      if (n + 1 < ntiles) step(n + 1, sK1, sV1, sK0, sV0);
+    }
+
+    // boundary: claim and stage the next item here if no tile did, build
+    // its list (nothing of this item reads LDS any more), then store this
+    // item's output, whose writes drain during the next item's first copy
+    if (!staged) {
+      if (ntiles == 0) {
+        if (tid == 0) s_next[0] = fetch();
+        __syncthreads();
+      }
+      nxt = __builtin_amdgcn_readfirstlane(s_next[0]);
+      if (nxt != kNoItem) stage(nxt);
+      wait_vmem();
+      __syncthreads();
+    }
+    if (nxt != kNoItem) nkb = build_list(nxt);
+    if (rows_valid) {
+      const float ltot = lsum + __shfl_xor(lsum, 32);
+      const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+      uint16_t* op = p.O + ((size_t)h * p.L + qrow) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int col = dt * 32 + 8 * gg + 4 * hi;
+          u32x2_t v;
+          v[0] = cvt2_bf16(o[dt][4 * gg] * inv, o[dt][4 * gg + 1] * inv);
+          v[1] = cvt2_bf16(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
+          *(u32x2_t*)(op + col) = v;
+        }
+    }
+    cur = nxt;
+    if (cur == kNoItem) break;
+  }
+}
+
 // dynamic LDS of the sparse mode: the merged block list, two bitmaps, offsets
 size_t list_bytes(int NB) {
   const int nw32 = (NB + 31) / 32;
   return (size_t)(NB + 3 * nw32 + 1) * sizeof(int32_t);
 }
 
+// This device's address of the work queues, looked up once per device with
+// that device current (concurrent first calls all store the same address).
+hipError_t queue_base(unsigned int** out) {
+  static std::atomic<unsigned int*> cached[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  unsigned int* ptr = cached[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* v = nullptr;
+    e = hipGetSymbolAddress(&v, HIP_SYMBOL(attn_queue));
+    if (e != hipSuccess) return e;
+    if (v == nullptr) return hipErrorInvalidSymbol;
+    ptr = (unsigned int*)v;
+    cached[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
+}
+
+// Queue slot of the next persistent launch (shared by every instantiation).
+std::atomic<unsigned int> next_queue_slot{0};
+
+// Sparse mode with index rows that fit the stage runs persistent (one
+// work-group per CU); dense mode and longer rows run one work-group per item.
 template <int D, int BQ>
-hipError_t launch(const FlashParams& fp, hipStream_t st) {
+hipError_t launch(FlashParams fp, hipStream_t st) {
   const size_t dyn = fp.idx ? list_bytes(fp.NB) : 0;
+  if (fp.idx != nullptr && fp.NB <= kRowAhead * BQ * 4) {
+    unsigned int* base = nullptr;
+    hipError_t e = queue_base(&base);
+    if (e != hipSuccess) return e;
+    const unsigned int slot = next_queue_slot.fetch_add(1u, std::memory_order_relaxed) % kQueueSlots;
+    fp.queue = base + (size_t)slot * kNumXcd * kQueueStride;
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, fp.queue);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((flash_bf16_persistent_kernel<D, BQ>), dim3(kNumXcd * cus_per_xcd()), dim3(BQ * 4),
+                       dyn, st, fp);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 4), dyn, st, fp);
   return hipGetLastError();
 }
@@ -563,6 +929,7 @@ hipError_t launch_flash_bf16(const Shape& s, const void* Q, const void* K, const
   fp.chunk_pairs = pairs_per_chunk(npairs);
   fp.interleave = (npairs * fp.group) % (kNumXcd * fp.chunk_pairs * fp.group) == 0;
   fp.scale_log2 = (float)(1.4426950408889634 / __builtin_sqrt((double)s.d));
+  fp.queue = nullptr;
   if (s.d == 128) return B == 128 ? launch<128, 128>(fp, st) : launch<128, 64>(fp, st);
   return B == 128 ? launch<64, 128>(fp, st) : launch<64, 64>(fp, st);
 }

@@ -13,6 +13,9 @@ struct Shape {
   bool bf16;
 };
 
+// Compute units per XCD of the current device (cached per device).
+int cus_per_xcd();
+
 // ---- block scores ---------------------------------------------------------
 // Workspace of the bf16 scoring path: per (head, 32-row group of reshaped rows)
 //   P: [NB][32] fp32 partial block sums (each against its own snapshot max)

@@ -677,24 +677,6 @@ hipError_t launch_gemm_bs(const GemmParams& gp, int bs, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// Compute units per XCD of the current device (the persistent GEMM runs one
-// workgroup per CU).  Cached per device; several host threads may fill an
-// entry at once, all with the same value, so relaxed atomics suffice.
-int cus_per_xcd() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
-  int v = cached[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kNumXcd)
-      n = 256;
-    v = n / kNumXcd;
-    cached[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
 struct WsLayout {
   size_t p_elems, m_elems;
   int Lr, NB, nR32, nct;
@@ -720,6 +702,24 @@ WsLayout ws_layout(const Shape& s, int S, int B) {
 static __device__ __align__(256) unsigned char scratch[kScoreScratchBytes];
 
 }  // namespace
+
+// Compute units per XCD of the current device (the persistent kernels run one
+// workgroup per CU).  Cached per device; several host threads may fill an
+// entry at once, all with the same value, so relaxed atomics suffice.
+int cus_per_xcd() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kNumXcd)
+      n = 256;
+    v = n / kNumXcd;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 hipError_t score_scratch_ptr(void** out) {
   static std::atomic<void*> cached[64];

@@ -259,6 +259,13 @@ xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, in
  * d = 128: NB <= 7488, i.e. L <= 958464; more: XATTN_EUNSUPPORTED); fp32
  * kernels cover d in {32, 64, 128}, B <= 256, and NB whose block bitmap fits
  * in LDS beside the fp32 tiles (else XATTN_EUNSUPPORTED).
+ * Concurrency: for bf16 with NB <= 16 B (index rows of at most four entries
+ * per thread), the call runs one persistent work-group per CU that takes
+ * work items from counters in a static device array of 64 launch slots,
+ * used round robin.  Calls on one GPU may run concurrently on different
+ * streams as long as fewer than 64 of them are in flight at once.  A captured
+ * graph replays the slot it was captured with, so two replays of one graph
+ * must not overlap.
  */
 xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
                                   const void* V, int32_t B, const int32_t* idx,
