@@ -600,17 +600,18 @@ constexpr int kRowAhead = 4;
 // A work item of the persistent kernel: (queue << 24) | index in that queue.
 constexpr int kNoItem = -1;
 
-// Persistent form of the sparse mode, for index rows of at most kRowAhead x
-// threads entries.  One work-group per CU takes the work items of its XCD
-// from a counter, in the non-persistent kernel's order; once that queue is
-// empty it takes the remaining items of the other XCDs' queues, so the load
-// stays balanced as with hardware dispatch.  What a work-group otherwise
-// pays at each start is hidden: near the end of item i the next item is
-// claimed and its index rows and counts are copied into LDS by direct-to-LDS
-// loads, so between two items only the list build from LDS, the query loads
-// and the first tile's copy remain.  Items, tiles and arithmetic are
-// those of the non-persistent kernel.
-template <int D, int BQ>
+// Persistent form of the kernel: dense mode, and sparse mode for index rows
+// of at most kRowAhead x threads entries.  One work-group per CU takes the
+// work items of its XCD from a counter, in the non-persistent kernel's
+// order; once that queue is empty it takes the remaining items of the other
+// XCDs' queues, so the load stays balanced as with hardware dispatch.  What
+// a work-group otherwise pays at each start is hidden: near the end of item
+// i the next item is claimed and (sparse mode) its index rows and counts are
+// copied into LDS by direct-to-LDS loads, so between two items only the list
+// build from LDS, the query loads and the first tile's copy remain.  Items,
+// tiles and arithmetic are those of the non-persistent kernel, which serves
+// longer index rows.
+template <int D, int BQ, bool SPARSE>
 __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashParams p) {
   constexpr int kBlockWaves = BQ / 32;
   constexpr int kWaves = 2 * kBlockWaves;
@@ -625,8 +626,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
   __shared__ __attribute__((aligned(1024))) uint8_t sV1[kTileBytes];
   // the next item's two index rows (adjacent in memory, copied as one run)
   // and its two counts; every lane of a copy writes, so the counts take 64
-  __shared__ __attribute__((aligned(256))) int32_t s_stage[kStageInts];
-  __shared__ __attribute__((aligned(256))) int32_t s_stage_cnt[64];
+  __shared__ __attribute__((aligned(256))) int32_t s_stage[SPARSE ? kStageInts : 1];
+  __shared__ __attribute__((aligned(256))) int32_t s_stage_cnt[SPARSE ? 64 : 1];
   __shared__ int s_next[2];
 
   const int tid = threadIdx.x;
@@ -680,47 +681,54 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
     qbA = 2 * (npairs - 1 - rem / p.group);
     h = g * p.group + rem % p.group;
   };
-  // copy item k's index rows and counts into the stage
+  // copy item k's index rows and counts into the stage (sparse mode)
   auto stage = [&](int k) __attribute__((always_inline)) {
-    int g, h, qbA;
-    locate(k, g, h, qbA);
-    const int rows = qbA + 1 < p.NB ? 2 : 1;
-    const int n = rows * p.NB;
-    const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.idx + ((size_t)h * p.NB + qbA) * p.NB), (short)0, n * 4, 0x00020000);
-    for (int i = wave; i < (n + 63) / 64; i += kWaves)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (__attribute__((address_space(3))) void*)(s_stage + i * 64),
-                                               4, lane * 4, i * 256, 0, 0);
-    if (wave == kWaves - 1) {
-      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(p.counts + (size_t)h * p.NB + qbA), (short)0, rows * 4, 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)s_stage_cnt, 4,
-                                               lane * 4, 0, 0, 0);
+    if constexpr (SPARSE) {
+      int g, h, qbA;
+      locate(k, g, h, qbA);
+      const int rows = qbA + 1 < p.NB ? 2 : 1;
+      const int n = rows * p.NB;
+      const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.idx + ((size_t)h * p.NB + qbA) * p.NB), (short)0, n * 4, 0x00020000);
+      for (int i = wave; i < (n + 63) / 64; i += kWaves)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ri, (__attribute__((address_space(3))) void*)(s_stage + i * 64),
+                                                 4, lane * 4, i * 256, 0, 0);
+      if (wave == kWaves - 1) {
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.counts + (size_t)h * p.NB + qbA), (short)0, rows * 4, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (__attribute__((address_space(3))) void*)s_stage_cnt, 4,
+                                                 lane * 4, 0, 0, 0);
+      }
     }
   };
-  // the merged list of item k from the stage (the bitmaps are clear on entry
-  // and cleared again as the list is written); returns the entry count
+  // sparse mode: the merged list of item k from the stage (the bitmaps are
+  // clear on entry and cleared again as the list is written); dense mode:
+  // every causal-visible key block.  Returns the number of key blocks.
   auto build_list = [&](int k) __attribute__((always_inline)) -> int {
     int g, h, qbA;
     locate(k, g, h, qbA);
     const int qbB = qbA + 1;
-    int cntA = s_stage_cnt[0];
-    int cntB = qbB < p.NB ? s_stage_cnt[1] : 0;
-    cntA = cntA < 0 ? 0 : (cntA > p.NB ? p.NB : cntA);
-    cntB = cntB < 0 ? 0 : (cntB > p.NB ? p.NB : cntB);
-    auto mark = [&](int kb, int b, int qbb) __attribute__((always_inline)) {
-      if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) return;
-      atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
-    };
+    if constexpr (SPARSE) {
+      int cntA = s_stage_cnt[0];
+      int cntB = qbB < p.NB ? s_stage_cnt[1] : 0;
+      cntA = cntA < 0 ? 0 : (cntA > p.NB ? p.NB : cntA);
+      cntB = cntB < 0 ? 0 : (cntB > p.NB ? p.NB : cntB);
+      auto mark = [&](int kb, int b, int qbb) __attribute__((always_inline)) {
+        if (kb < 0 || kb >= p.NB || (p.causal && kb > qbb)) return;
+        atomicOr(&s_bits[b * nw32 + (kb >> 5)], 1u << (kb & 31));
+      };
 #pragma unroll
-    for (int m = 0; m < kRowAhead; ++m) {
-      const int j = tid + m * kThreads;
-      if (j < cntA) mark(s_stage[j], 0, qbA);
-      if (j < cntB) mark(s_stage[p.NB + j], 1, qbB);
+      for (int m = 0; m < kRowAhead; ++m) {
+        const int j = tid + m * kThreads;
+        if (j < cntA) mark(s_stage[j], 0, qbA);
+        if (j < cntB) mark(s_stage[p.NB + j], 1, qbB);
+      }
+      __syncthreads();
+      finish_list<kThreads>(s_bits, s_off, s_list, nw32, tid, wave, lane, true);
+      return s_off[nw32];
+    } else {
+      return p.causal ? min(qbB, p.NB - 1) + 1 : p.NB;
     }
-    __syncthreads();
-    finish_list<kThreads>(s_bits, s_off, s_list, nw32, tid, wave, lane, true);
-    return s_off[nw32];
   };
 
   // The first item; its number reaches every thread through LDS.  Each later
@@ -730,7 +738,8 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
   // during the tile after the claim.
   constexpr int kClaimAhead = 3;
   if (tid == 0) s_next[0] = fetch();
-  for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
+  if constexpr (SPARSE)
+    for (int i = tid; i < 2 * nw32; i += kThreads) s_bits[i] = 0u;
   __syncthreads();
   int cur = __builtin_amdgcn_readfirstlane(s_next[0]);
   if (cur == kNoItem) return;
@@ -760,9 +769,17 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
 
     const int ntiles = nkb * kTilesPerBlock;
     auto tile_info = [&](int n, bool& mine) -> int {
-      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_list[n / kTilesPerBlock]);
-      mine = half ? (e >> 31) : ((e >> 30) & 1u);
-      return (int)(e & 0x3FFFFFFFu) * BQ + (n % kTilesPerBlock) * kKT;
+      const int j = n / kTilesPerBlock;
+      int kb;
+      if constexpr (SPARSE) {
+        const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(s_list[j]);
+        mine = half ? (e >> 31) : ((e >> 30) & 1u);
+        kb = (int)(e & 0x3FFFFFFFu);
+      } else {
+        kb = j;
+        mine = half ? (qbA + 1 < p.NB && (!p.causal || kb <= qbA + 1)) : (!p.causal || kb <= qbA);
+      }
+      return kb * BQ + (n % kTilesPerBlock) * kKT;
     };
 
     f32x16_t o[D / 32];
@@ -878,12 +895,13 @@ hipError_t queue_base(unsigned int** out) {
 // Queue slot of the next persistent launch (shared by every instantiation).
 std::atomic<unsigned int> next_queue_slot{0};
 
-// Sparse mode with index rows that fit the stage runs persistent (one
-// work-group per CU); dense mode and longer rows run one work-group per item.
+// Dense mode, and sparse mode with index rows that fit the stage, run
+// persistent (one work-group per CU); longer index rows run one work-group
+// per item.
 template <int D, int BQ>
 hipError_t launch(FlashParams fp, hipStream_t st) {
   const size_t dyn = fp.idx ? list_bytes(fp.NB) : 0;
-  if (fp.idx != nullptr && fp.NB <= kRowAhead * BQ * 4) {
+  if (fp.idx == nullptr || fp.NB <= kRowAhead * BQ * 4) {
     unsigned int* base = nullptr;
     hipError_t e = queue_base(&base);
     if (e != hipSuccess) return e;
@@ -892,8 +910,12 @@ hipError_t launch(FlashParams fp, hipStream_t st) {
     hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, st, fp.queue);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((flash_bf16_persistent_kernel<D, BQ>), dim3(kNumXcd * cus_per_xcd()), dim3(BQ * 4),
-                       dyn, st, fp);
+    if (fp.idx != nullptr)
+      hipLaunchKernelGGL((flash_bf16_persistent_kernel<D, BQ, true>), dim3(kNumXcd * cus_per_xcd()),
+                         dim3(BQ * 4), dyn, st, fp);
+    else
+      hipLaunchKernelGGL((flash_bf16_persistent_kernel<D, BQ, false>), dim3(kNumXcd * cus_per_xcd()),
+                         dim3(BQ * 4), dyn, st, fp);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((flash_bf16_kernel<D, BQ>), dim3(fp.grid), dim3(BQ * 4), dyn, st, fp);

@@ -37,10 +37,15 @@
  *     error has enqueued nothing, except XATTN_EHIP (a launch failed).
  *     xattn_last_error() returns a thread-local description of the last
  *     error.  No C++ exception crosses this interface.
- *   - Calls keep no mutable global state apart from a per-device cache of
- *     the compute-unit count (filled once, atomically) and the thread-local
- *     error string, and are safe to issue from several host threads; calls
- *     on one stream run in order.
+ *   - Mutable global state is limited to four things:
+ *     - per-device caches of the compute-unit count and of two static device
+ *       arrays' addresses, each filled once, atomically;
+ *     - the work-item counters of the bf16 attention calls: 64 launch slots,
+ *       used round robin (see xattn_sparse_prefill);
+ *     - the scratch of xattn_score_noalloc;
+ *     - the thread-local error string.
+ *     Calls are safe to issue from several host threads; calls on one stream
+ *     run in order.
  */
 #ifndef XATTN_H
 #define XATTN_H
@@ -262,10 +267,10 @@ xattn_status xattn_tau_dp(int32_t hq, int32_t levels, const double* err_host, in
  * Concurrency: for bf16 with NB <= 16 B (index rows of at most four entries
  * per thread), the call runs one persistent work-group per CU that takes
  * work items from counters in a static device array of 64 launch slots,
- * used round robin.  Calls on one GPU may run concurrently on different
- * streams as long as fewer than 64 of them are in flight at once.  A captured
- * graph replays the slot it was captured with, so two replays of one graph
- * must not overlap.
+ * used round robin (shared with xattn_full).  Calls on one GPU may run
+ * concurrently on different streams as long as fewer than 64 of them are in
+ * flight at once.  A captured graph replays the slot it was captured with,
+ * so two replays of one graph must not overlap.
  */
 xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const void* K,
                                   const void* V, int32_t B, const int32_t* idx,
@@ -284,6 +289,9 @@ xattn_status xattn_sparse_prefill(const xattn_shape* shape, const void* Q, const
  *   O  out, [hq][L][d] in the input dtype, fully overwritten.
  * bf16 kernels need L % 64 == 0, d in {64, 128} and L * d * 2 < 2^31 bytes
  * per head; fp32 kernels cover d in {32, 64, 128} (else XATTN_EUNSUPPORTED).
+ * Concurrency: in bf16 the call runs the persistent kernel of
+ * xattn_sparse_prefill and shares its 64 launch slots, with the same limit
+ * on calls in flight at once.
  */
 xattn_status xattn_full(const xattn_shape* shape, const void* Q, const void* K,
                         const void* V, void* O, void* stream);
