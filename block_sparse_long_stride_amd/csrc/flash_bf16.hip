@@ -848,17 +848,40 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
     if (rows_valid) {
       const float ltot = lsum + __shfl_xor(lsum, 32);
       const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-      uint16_t* op = p.O + ((size_t)h * p.L + qrow) * D;
+      // this wave's 32 x D output through LDS (the second K/V buffer is free
+      // here): written in the accumulator layout with 16-byte chunks
+      // XOR-swizzled by row, read back row by row, stored as whole rows
+      constexpr int kRowB = D * 2;                  // bytes per output row
+      constexpr int kChunks = kRowB / 16;
+      // a lane index the compiler cannot see through, so the addresses below
+      // are formed here rather than held in registers across the item loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int r32 = ln & 31, hh = ln >> 5;
+      // a K or V buffer holds kKT / 32 waves' 32-row tiles, the two hold all waves
+      constexpr int kWavesPerBuf = kKT / 32;
+      static_assert(2 * kWavesPerBuf >= kWaves && kWavesPerBuf * 32 * kRowB <= kTileBytes,
+                    "output tiles fit the second K/V buffer pair");
+      uint8_t* ot = (wave < kWavesPerBuf ? sK1 : sV1) + (wave % kWavesPerBuf) * (32 * kRowB);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-          const int col = dt * 32 + 8 * gg + 4 * hi;
+          const int col = dt * 32 + 8 * gg;         // 8-element chunk; this lane holds half 4 hi .. +4
           u32x2_t v;
           v[0] = cvt2_bf16(o[dt][4 * gg] * inv, o[dt][4 * gg + 1] * inv);
           v[1] = cvt2_bf16(o[dt][4 * gg + 2] * inv, o[dt][4 * gg + 3] * inv);
-          *(u32x2_t*)(op + col) = v;
+          const int ch = (col / 8) ^ (r32 % kChunks);
+          *(u32x2_t*)(ot + r32 * kRowB + ch * 16 + 8 * hh) = v;
         }
+      constexpr int kRowsPerInst = 64 / kChunks;
+      uint16_t* op = p.O + ((size_t)h * p.L + qwave0) * D;
+#pragma unroll
+      for (int i = 0; i < 32 / kRowsPerInst; ++i) {
+        const int r = i * kRowsPerInst + ln / kChunks, c = ln % kChunks;
+        const u32x4_t v = *(const u32x4_t*)(ot + r * kRowB + ((c ^ (r % kChunks)) * 16));
+        *(u32x4_t*)(op + (size_t)r * D + c * 8) = v;
+      }
     }
     cur = nxt;
     if (cur == kNoItem) break;
