@@ -760,12 +760,26 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
     const __amdgpu_buffer_rsrc_t Vg = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.V + (size_t)g * p.L * D), (short)0, p.L * D * 2, 0x00020000);
 
+    // This wave's 32 query rows (contiguous in memory) by direct-to-LDS
+    // copies into its slot of the second buffer pair, which is free until the
+    // first tile's barrier, in the key tiles' swizzled layout; the fragments
+    // are then read with the key-fragment offsets.  Per-lane fragment loads
+    // from memory would touch 32 rows per instruction and hold up the tile
+    // copies queued behind them.
+    constexpr int kWavesPerBuf = kKT / 32;   // 32-row slots per K or V buffer
+    static_assert(2 * kWavesPerBuf >= kWaves && kWavesPerBuf * 32 * D * 2 <= kTileBytes,
+                  "query rows fit the second K/V buffer pair");
+    const __amdgpu_buffer_rsrc_t Qw = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.Q + ((size_t)h * p.L + (rows_valid ? qwave0 : qwave0 - BQ)) * D), (short)0, 32 * D * 2,
+        0x00020000);
+    // (The lane index goes through an opaque copy so that the eight per-lane
+    // offsets are recomputed per item rather than kept live across the loop,
+    // where they would be spilled and reloaded before the copies.)
+    int qln = lane;
+    asm volatile("" : "+v"(qln));
+    if (wave < kWavesPerBuf) load_tile<D, 32, 1>(Qw, 0, sK1 + (wave % kWavesPerBuf) * (32 * D * 2), 0, qln);
+    else load_tile<D, 32, 1>(Qw, 0, sV1 + (wave % kWavesPerBuf) * (32 * D * 2), 0, qln);
     bf16x8_t qf[D / 16];
-    {
-      const uint16_t* qp = p.Q + ((size_t)h * p.L + (rows_valid ? qrow : qrow - BQ)) * D + hi * 8;
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qp + 16 * t));
-    }
 
     const int ntiles = nkb * kTilesPerBlock;
     auto tile_info = [&](int n, bool& mine) -> int {
@@ -801,6 +815,15 @@ __global__ __launch_bounds__(BQ * 4, 1) void flash_bf16_persistent_kernel(FlashP
       load_tile<D, kKT, kWaves>(Vg, key0, sV0, wave, lane);
     }
     wait_vmem();
+    // the wave's own query rows have landed: read its fragments before the
+    // barrier, after which tile 1 is copied over them
+    auto read_q = [&](const uint8_t* buf) __attribute__((always_inline)) {
+      const uint8_t* qs = buf + (wave % kWavesPerBuf) * (32 * D * 2);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) qf[t] = as_bf16x8(*(const u32x4_t*)(qs + koff[t]));
+    };
+    if (wave < kWavesPerBuf) read_q(sK1);
+    else read_q(sV1);
     __syncthreads();
 
     auto step = [&](int n, const uint8_t* sK, const uint8_t* sV, uint8_t* nK,
